@@ -1,0 +1,306 @@
+"""Throughput of the decode hot path (store + decode_rows + index score/top-k + sparse
+attend) on one MI355X, on seeded synthetic inputs shaped like the pages' workloads.
+
+One step = one sparse layer's full path for one batch: m3s_store of the step's new
+K/V/index rows, m3s_decode_rows, m3s_index_topk, m3s_sparse_attend. Steps are HIP-graph
+replays; consecutive steps use different layer copies of the cache (8 by default, >= 2 GB
+in total at the default workload) so a step cannot be served from the 256 MB Infinity
+Cache left warm by the previous one - as in a real model, where each of the 60 sparse
+layers has its own cache.
+
+Prints ONE JSON line (stdout). Extra detail goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode rows/s + achieved HBM GB/s (store+score+top-k+attend), 8 req x 8 rows @150K"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_topk_b8x8_150k_traffic.json")
+INDEX_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/index_topk.hip", "block_sparse_decode_nvfp4_amd/csrc/fp4.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def step_bytes(cfg, lay, ids_np, G):
+    import numpy as np
+    rb = 72 if cfg.fmt == "nvfp4" else 68
+    R = int(lay.cu_q[-1])
+    seq = lay.seq_lens.astype(np.int64)
+    index = int(seq.sum()) * rb                                   # every causal index token
+    pairs = set()
+    row_req = np.repeat(np.arange(len(seq)), np.diff(lay.cu_q))
+    for r in range(R):
+        for j in ids_np[r]:
+            if j >= 0:
+                pairs.add((int(row_req[r]), int(j)))
+    attend = 0
+    for b, j in pairs:                                             # distinct (request, block) K+V
+        attend += 2 * rb * min(128, int(seq[b]) - 128 * j)
+    T = R
+    store = T * 3 * 256 + T * 3 * rb                               # read bf16 rows, write planes
+    tables = int(((seq + 127) // 128).sum()) * 4                   # causal block-table entries
+    queries = R * 256 + R * G * 256                                # q_idx + q (bf16)
+    outs = R * G * 128 * 4 + 2 * R * cfg.topk * 4                  # fp32 out + ids (write + read)
+    other = store + tables + queries + outs
+    return {"index": index, "attend": attend, "store": store, "other": other,
+            "total": index + attend + other, "index_call": index + tables + R * 256}
+
+
+def cpu_baseline(cfg, case, nreq, log_fn):
+    """The oracle as it stands, timed on the host on `nreq` whole requests of the workload."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from oracle import path as P
+
+    lay = case.layout
+    reqs = list(range(nreq))
+    # untimed: the oracle's own planes for the sampled requests' history
+    planes = P.new_planes(cfg.fmt, lay.num_pages)
+    slots = W.all_slots(lay)
+    new = set(lay.new_tokens.tolist())
+    new_rows = {}
+    for b in reqs:
+        lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
+        keep = np.array([t not in new for t in range(lo, hi)])
+        P.store(planes, cfg.fmt, {n: W.bf16_bits(getattr(case, n)[lo:hi])[keep] for n in ("k", "v", "idx")},
+                slots[lo:hi][keep])
+    nt = lay.new_tokens
+    sel = np.concatenate([np.arange(int(lay.cu_q[b]), int(lay.cu_q[b + 1])) for b in reqs])
+    for n in ("k", "v", "idx"):
+        t = getattr(case, n)
+        new_rows[n] = W.bf16_bits(t[torch.as_tensor(nt[sel], device=t.device)])
+    q_idx = W.bf16_bits(case.q_idx)
+    q = W.bf16_bits(case.q)
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    P.step(planes, cfg.fmt, new_rows, lay.new_slots[sel], lay.cu_q, lay.seq_lens, lay.block_table,
+           q_idx, q, cfg.topk, cfg.sm_scale, requests=reqs)
+    dt = time.perf_counter() - t0
+    rows = int(sum(int(lay.cu_q[b + 1] - lay.cu_q[b]) for b in reqs))
+    log_fn(f"[cpu baseline] oracle step on {nreq} request(s) ({rows} rows): {dt:.2f} s")
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{nreq} of {len(lay.seq_lens)} requests ({rows} rows) of the same workload, full step "
+                      f"(store of their rows, row map, float64 dequantize + score of every causal block, "
+                      f"sort top-k, float64 softmax attention), history quantization untimed; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", default="b8x8_150k")
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--cpu-requests", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=50)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the path is one GPU's share (one KV head, one TP rank); "
+              f"--gpus {args.gpus} / WORLD_SIZE {world} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_decode_nvfp4_amd as m3s
+    import workloads as W
+
+    m3s.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.config(int(args.config) if args.config.isdigit() else args.config)
+    log(f"[bench] workload {cfg.name}: {cfg.description}")
+    t_setup = time.perf_counter()
+    case = W.make_case(cfg, dev)
+    lay = case.layout
+    R = int(lay.cu_q[-1])
+    G = case.q.shape[1]
+    NL = max(1, args.layers)
+
+    # ---- per-layer caches, history stored by the library (untimed setup)
+    slots_all = torch.as_tensor(W.all_slots(lay), device=dev)
+    hist = torch.ones(lay.total_tokens, dtype=torch.bool, device=dev)
+    new_idx = torch.as_tensor(lay.new_tokens, device=dev)
+    hist[new_idx] = False
+    hidx = torch.nonzero(hist).flatten()
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    caches = []
+    for L in range(NL):
+        c = m3s.Cache(cfg.fmt, lay.num_pages, dev)
+        for s in range(0, hidx.numel(), 1 << 20):
+            h = hidx[s: s + (1 << 20)]
+            m3s.m3s_store(c, case.k[h], case.v[h], case.idx[h], slots_all[h].contiguous(), status)
+        caches.append(c)
+    torch.cuda.synchronize()
+
+    # ---- static step buffers
+    k_new = case.k[new_idx].contiguous()
+    v_new = case.v[new_idx].contiguous()
+    i_new = case.idx[new_idx].contiguous()
+    s_new = slots_all[new_idx].contiguous()
+    cu_q = torch.as_tensor(lay.cu_q, device=dev)
+    seq = torch.as_tensor(lay.seq_lens, device=dev)
+    bt = torch.as_tensor(lay.block_table, device=dev)
+    row_req = torch.empty(R, dtype=torch.int32, device=dev)
+    row_len = torch.empty(R, dtype=torch.int32, device=dev)
+    req_blk = torch.empty(len(lay.seq_lens) + 1, dtype=torch.int32, device=dev)
+    rows = m3s.m3s_decode_rows(cu_q, seq, R, row_req, row_len, req_blk, status)
+    ids = torch.empty((R, cfg.topk), dtype=torch.int32, device=dev)
+    out = torch.empty((R, G, 128), dtype=torch.float32, device=dev)
+    ws_i = m3s.index_workspace(rows, lay.max_blocks, cfg.topk, dev)
+    ws_a = m3s.attend_workspace(rows, lay.max_blocks, cfg.topk, G, dev)
+
+    def run_step(c, evs=None):
+        if evs:
+            evs[0].record()
+        m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
+        if evs:
+            evs[1].record()
+        m3s.m3s_decode_rows(cu_q, seq, R, row_req, row_len, req_blk, status)
+        if evs:
+            evs[2].record()
+        m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0, ids, ws_i, status)
+        if evs:
+            evs[3].record()
+        m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids, cfg.sm_scale, out, ws_a, status)
+        if evs:
+            evs[4].record()
+
+    for c in caches:  # eager warm-up, checks the status word
+        run_step(c)
+    torch.cuda.synchronize()
+    st = int(status.item())
+    if st:
+        log(f"[bench] device status {st:#x}")
+        sys.exit(3)
+
+    # ---- graphs: one per layer, with HIP event records between the stages
+    side = torch.cuda.Stream()
+    graphs, evsets, staged = [], [], True
+    for c in caches:
+        g = torch.cuda.CUDAGraph()
+        evs = None
+        try:
+            evs = [torch.cuda.Event(enable_timing=True, external=True) for _ in range(5)]
+        except TypeError:
+            staged = False
+        with torch.cuda.graph(g, stream=side):
+            run_step(c, evs if staged else None)
+        graphs.append(g)
+        evsets.append(evs)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; {NL} layers x {lay.num_pages} pages; "
+        f"rows {R}, G {G}, top-k {cfg.topk}")
+
+    # ---- timed region: K steps, graph replays cycling over the layers
+    for i in range(args.warmup):
+        graphs[i % NL].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % NL].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / args.steps
+    st = int(status.item())
+
+    # ---- per-stage HIP-event times (graph replays, one layer each, synchronized)
+    stage_ms = None
+    if staged and evsets[0] is not None:
+        acc = np.zeros(4)
+        n = 0
+        for i in range(args.stage_reps):
+            L = (i + 3) % NL
+            graphs[L].replay()
+            torch.cuda.synchronize()
+            evs = evsets[L]
+            acc += [evs[j].elapsed_time(evs[j + 1]) for j in range(4)]
+            n += 1
+        stage_ms = (acc / n).tolist()
+
+    ids_np = ids.cpu().numpy()
+    by = step_bytes(cfg, lay, ids_np, G)
+    rows_per_s = R / (ms_per_step / 1e3)
+    gbs_step = by["total"] / (ms_per_step / 1e3) / 1e9
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (event), wall {wall / args.steps * 1e6:.2f} us/step")
+    log(f"[bench] algorithmic bytes/step: index {by['index'] / 1e6:.2f} MB, attend {by['attend'] / 1e6:.2f} MB, "
+        f"other {by['other'] / 1e6:.2f} MB, total {by['total'] / 1e6:.2f} MB -> {gbs_step:.0f} GB/s")
+    roofline = None
+    if stage_ms:
+        names = ["store", "decode_rows", "index_topk", "sparse_attend"]
+        log("[bench] stages (us): " + ", ".join(f"{nm} {v * 1e3:.2f}" for nm, v in zip(names, stage_ms)))
+        t_idx = stage_ms[2] / 1e3
+        ach = by["index_call"] / t_idx / 1e9
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            try:
+                tf = json.load(open(TRAFFIC_FILE))
+                if tf.get("source_sha") == source_sha(INDEX_SOURCES) and tf.get("workload") == cfg.name:
+                    traffic = tf.get("bytes_per_launch")
+            except Exception:
+                traffic = None
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "m3s_index_topk (index_scan + index_select kernels)",
+                    "launch_us": round(stage_ms[2] * 1e3, 2), "bytes_per_launch": by["index_call"]}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, case, args.cpu_requests, log)
+
+    res = {
+        "metric": METRIC,
+        "value": round(rows_per_s, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "requests": len(lay.seq_lens), "rows_per_request": cfg.q_len,
+                   "context": [int(x) for x in sorted(set(lay.seq_lens.tolist()))][:4],
+                   "heads_per_kv_head": G, "topk": cfg.topk, "cache_format": cfg.fmt, "layers_cycled": NL},
+        "hbm_gbs_step": round(gbs_step, 1),
+        "bytes_per_step": by["total"],
+        "stage_us": None if not stage_ms else [round(v * 1e3, 2) for v in stage_ms],
+        "device_status": st,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

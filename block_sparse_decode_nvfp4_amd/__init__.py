@@ -1,0 +1,265 @@
+"""Python binding of libm3s.so, the MI355X decode hot path for block-sparse
+attention over NVFP4 / MXFP4 paged caches.
+
+This module only marshals arguments (torch tensors -> device pointers, the
+current HIP stream) into the C ABI declared in include/m3s.h; every step of
+the path runs in the library's HIP kernels. Loading fails loudly when the
+library is missing: there is no fallback.
+
+Functions carry the C names: m3s_store, m3s_decode_rows, m3s_index_topk,
+m3s_sparse_attend, m3s_workspace_bytes, m3s_read_device_status,
+m3s_status_string, m3s_version.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libm3s.so")
+
+PAGE = 128
+HEAD_DIM = 128
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+FMT_NVFP4, FMT_MXFP4 = 1, 2
+FORMATS = {"nvfp4": FMT_NVFP4, "mxfp4": FMT_MXFP4}
+SCALE_BYTES = {FMT_NVFP4: 8, FMT_MXFP4: 4}
+OP_INDEX_TOPK, OP_SPARSE_ATTEND = 1, 2
+TOPK_TIE_HIGH_ID = 1
+DEV_BITS = {
+    "BAD_SLOT": 1 << 0, "BAD_ROWS": 1 << 1, "BAD_LENGTH": 1 << 2, "BAD_PAGE": 1 << 3,
+    "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6,
+}
+
+EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_index_topk", "m3s_sparse_attend",
+           "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
+
+_c_i32p = ctypes.c_void_p
+_lib = None
+
+
+class M3SError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: status {status}: {m3s_status_string(status)}")
+
+
+class m3s_cache(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("k_data", ctypes.c_void_p), ("k_scale", ctypes.c_void_p),
+                ("v_data", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("idx_data", ctypes.c_void_p), ("idx_scale", ctypes.c_void_p)]
+
+
+class m3s_rows(ctypes.Structure):
+    _fields_ = [("cu_q", ctypes.c_void_p), ("row_req", ctypes.c_void_p), ("row_len", ctypes.c_void_p),
+                ("req_blk", ctypes.c_void_p), ("num_reqs", ctypes.c_int32), ("num_rows", ctypes.c_int32)]
+
+
+def load(path: str | None = None):
+    """Load libm3s.so (raises if it is missing or not loadable)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
+                           "or python block_sparse_decode_nvfp4_amd/_build.py")
+    lib = ctypes.CDLL(p)
+    V, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "m3s_store": (I32, [V, V, V, V, I64, V, I32, V, V]),
+        "m3s_decode_rows": (I32, [V, V, I32, I32, V, V, V, V, V]),
+        "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, V, V, SZ, V, V]),
+        "m3s_sparse_attend": (I32, [V, V, I64, I64, I32, V, I32, I32, V, V, I32, F32, V, V, SZ, V, V]),
+        "m3s_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
+        "m3s_read_device_status": (I32, [V, V, V]),
+        "m3s_status_string": (ctypes.c_char_p, [I32]),
+        "m3s_version": (I32, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, st):
+    if st != OK:
+        raise M3SError(fn, st)
+
+
+def _need(t, name, dtype, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def m3s_version() -> int:
+    return int(load().m3s_version())
+
+
+def m3s_status_string(status: int) -> str:
+    return load().m3s_status_string(int(status)).decode()
+
+
+def m3s_workspace_bytes(op: int, num_rows: int, num_reqs: int, max_blocks: int, topk: int, num_heads: int) -> int:
+    return int(load().m3s_workspace_bytes(op, num_rows, num_reqs, max_blocks, topk, num_heads))
+
+
+class Cache:
+    """One KV head's paged planes (k, v, index K; payload + scale each) on a device."""
+
+    def __init__(self, fmt: str, num_pages: int, device="cuda"):
+        torch = _torch()
+        self.fmt = fmt
+        self.format = FORMATS[fmt]
+        self.num_pages = int(num_pages)
+        sb = SCALE_BYTES[self.format]
+        self.planes = {}
+        for name in ("k", "v", "idx"):
+            self.planes[name] = (torch.zeros((num_pages, PAGE, 64), dtype=torch.uint8, device=device),
+                                 torch.zeros((num_pages, PAGE, sb), dtype=torch.uint8, device=device))
+        self._struct()
+
+    def _struct(self):
+        p = self.planes
+        self.c = m3s_cache(self.format, self.num_pages, PAGE, HEAD_DIM, 1,
+                           p["k"][0].data_ptr(), p["k"][1].data_ptr(), p["v"][0].data_ptr(), p["v"][1].data_ptr(),
+                           p["idx"][0].data_ptr(), p["idx"][1].data_ptr())
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+class Rows:
+    """The row map of one step (device tensors) and its m3s_rows struct."""
+
+    def __init__(self, cu_q, row_req, row_len, req_blk, num_reqs: int, num_rows: int):
+        self.cu_q, self.row_req, self.row_len, self.req_blk = cu_q, row_req, row_len, req_blk
+        self.num_reqs, self.num_rows = int(num_reqs), int(num_rows)
+        self.c = m3s_rows(cu_q.data_ptr(), row_req.data_ptr(), row_len.data_ptr(), req_blk.data_ptr(),
+                          self.num_reqs, self.num_rows)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def m3s_store(cache: Cache, k, v, idx, slot_mapping, dev_status=None, stream=None):
+    """Quantize bf16 rows [T, >=128] of k / v / idx (any may be None) into the planes at slot_mapping."""
+    torch = _torch()
+    ref = next(t for t in (k, v, idx) if t is not None)
+    T = ref.shape[0]
+    stride = ref.stride(0)
+    for name, t in (("k", k), ("v", v), ("idx", idx)):
+        if t is not None:
+            _need(t, name, torch.bfloat16)
+            if t.shape[0] != T or t.stride(0) != stride or t.stride(1) != 1 or t.shape[1] < HEAD_DIM:
+                raise ValueError(f"{name}: rows must share [T, >=128] shape and row stride")
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    if slot_mapping.numel() != T or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 [T]")
+    st = load().m3s_store(cache.ref(), _ptr(k), _ptr(v), _ptr(idx), stride, _ptr(slot_mapping), T,
+                          _ptr(dev_status), _stream(stream))
+    _check("m3s_store", st)
+
+
+def m3s_decode_rows(cu_q, seq_lens, num_rows: int, row_req=None, row_len=None, req_blk=None,
+                    dev_status=None, stream=None) -> Rows:
+    torch = _torch()
+    _need(cu_q, "cu_q", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    B = seq_lens.numel()
+    if cu_q.numel() != B + 1:
+        raise ValueError("cu_q must have num_reqs + 1 entries")
+    dev = cu_q.device
+    row_req = torch.empty(num_rows, dtype=torch.int32, device=dev) if row_req is None else row_req
+    row_len = torch.empty(num_rows, dtype=torch.int32, device=dev) if row_len is None else row_len
+    req_blk = torch.empty(B + 1, dtype=torch.int32, device=dev) if req_blk is None else req_blk
+    st = load().m3s_decode_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, _ptr(row_req), _ptr(row_len),
+                                _ptr(req_blk), _ptr(dev_status), _stream(stream))
+    _check("m3s_decode_rows", st)
+    return Rows(cu_q, row_req, row_len, req_blk, B, num_rows)
+
+
+def index_workspace(rows: Rows, max_blocks: int, topk: int, device="cuda"):
+    torch = _torch()
+    n = m3s_workspace_bytes(OP_INDEX_TOPK, rows.num_rows, rows.num_reqs, max_blocks, topk, 1)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def attend_workspace(rows: Rows, max_blocks: int, topk: int, num_heads: int, device="cuda"):
+    torch = _torch()
+    n = m3s_workspace_bytes(OP_SPARSE_ATTEND, rows.num_rows, rows.num_reqs, max_blocks, topk, num_heads)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def m3s_index_topk(cache: Cache, q_idx, block_table, max_blocks: int, rows: Rows, topk: int, flags: int = 0,
+                   topk_ids=None, workspace=None, dev_status=None, stream=None):
+    torch = _torch()
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    if q_idx.dim() != 2 or q_idx.stride(1) != 1 or q_idx.shape[1] < HEAD_DIM:
+        raise ValueError("q_idx must be [R, >=128] with unit inner stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, stride] with unit inner stride")
+    if topk_ids is None:
+        topk_ids = torch.empty((rows.num_rows, topk), dtype=torch.int32, device=q_idx.device)
+    if workspace is None:
+        workspace = index_workspace(rows, max_blocks, topk, q_idx.device)
+    st = load().m3s_index_topk(cache.ref(), _ptr(q_idx), q_idx.stride(0), _ptr(block_table), block_table.stride(0),
+                               max_blocks, rows.ref(), topk, flags, _ptr(topk_ids), _ptr(workspace),
+                               workspace.numel(), _ptr(dev_status), _stream(stream))
+    _check("m3s_index_topk", st)
+    return topk_ids
+
+
+def m3s_sparse_attend(cache: Cache, q, block_table, max_blocks: int, rows: Rows, topk_ids, sm_scale: float,
+                      out=None, workspace=None, dev_status=None, stream=None):
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    _need(topk_ids, "topk_ids", torch.int32)
+    if q.dim() != 3 or q.stride(2) != 1 or q.shape[2] < HEAD_DIM:
+        raise ValueError("q must be [R, G, >=128] with unit inner stride")
+    G = q.shape[1]
+    topk = topk_ids.shape[1]
+    if out is None:
+        out = torch.empty((rows.num_rows, G, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = attend_workspace(rows, max_blocks, topk, G, q.device)
+    st = load().m3s_sparse_attend(cache.ref(), _ptr(q), q.stride(0), q.stride(1), G, _ptr(block_table),
+                                  block_table.stride(0), max_blocks, rows.ref(), _ptr(topk_ids), topk,
+                                  float(sm_scale), _ptr(out), _ptr(workspace), workspace.numel(),
+                                  _ptr(dev_status), _stream(stream))
+    _check("m3s_sparse_attend", st)
+    return out
+
+
+def m3s_read_device_status(dev_status, stream=None) -> int:
+    out = ctypes.c_uint32(0)
+    st = load().m3s_read_device_status(_ptr(dev_status), ctypes.byref(out), _stream(stream))
+    _check("m3s_read_device_status", st)
+    return int(out.value)

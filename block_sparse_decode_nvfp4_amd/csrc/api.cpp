@@ -1,0 +1,244 @@
+// C-ABI entry points: synchronous host-side validation, then asynchronous
+// launches on the caller's stream. Nothing here allocates, frees or waits
+// (except m3s_read_device_status, which is documented to synchronize).
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../../include/m3s.h"
+#include "launch.hpp"
+
+using namespace m3s;
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+m3s_status check_cache(const m3s_cache* c) {
+  if (!c) return M3S_ERR_INVALID_ARG;
+  if (c->format != M3S_FMT_NVFP4 && c->format != M3S_FMT_MXFP4) return M3S_ERR_UNSUPPORTED;
+  if (c->page_size != M3S_PAGE || c->head_dim != M3S_HEAD_DIM || c->num_kv_heads != 1)
+    return M3S_ERR_UNSUPPORTED;
+  if (c->num_pages < 0) return M3S_ERR_INVALID_ARG;
+  return M3S_OK;
+}
+
+m3s_status check_rows(const m3s_rows* r) {
+  if (!r) return M3S_ERR_INVALID_ARG;
+  if (r->num_reqs < 0 || r->num_rows < 0) return M3S_ERR_INVALID_ARG;
+  if (r->num_reqs > M3S_MAX_REQS || r->num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
+  if (!r->cu_q || !r->req_blk) return M3S_ERR_INVALID_ARG;
+  if (r->num_rows > 0 && (!r->row_req || !r->row_len)) return M3S_ERR_INVALID_ARG;
+  return M3S_OK;
+}
+
+m3s_status check_table(const int32_t* bt, int32_t bt_stride, int32_t max_blocks) {
+  if (!bt) return M3S_ERR_INVALID_ARG;
+  if (max_blocks < 1 || bt_stride < max_blocks) return M3S_ERR_INVALID_ARG;
+  if (max_blocks > M3S_MAX_BLOCKS) return M3S_ERR_UNSUPPORTED;
+  return M3S_OK;
+}
+
+int scan_grid() {
+  static int cached = 0;
+  if (cached) return cached;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  cached = 8 * cus;
+  return cached;
+}
+
+m3s_status from_hip(hipError_t e) { return e == hipSuccess ? M3S_OK : M3S_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t m3s_version(void) { return M3S_VERSION; }
+
+const char* m3s_status_string(m3s_status s) {
+  switch (s) {
+    case M3S_OK: return "ok";
+    case M3S_ERR_INVALID_ARG: return "invalid argument (null pointer, negative count, bad stride or alignment)";
+    case M3S_ERR_UNSUPPORTED: return "unsupported shape (page/head_dim != 128, G, top-k, or size limits)";
+    case M3S_ERR_WORKSPACE: return "workspace null or smaller than m3s_workspace_bytes";
+    case M3S_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32_t max_blocks, int32_t topk,
+                           int32_t num_heads) {
+  (void)num_reqs;
+  (void)num_heads;
+  if (num_rows < 0 || max_blocks < 0 || topk < 1 || topk > M3S_MAX_TOPK) return 0;
+  if (op == M3S_OP_INDEX_TOPK) return index_ws_bytes(num_rows, max_blocks);
+  if (op == M3S_OP_SPARSE_ATTEND) return attend_ws_bytes(num_rows, attend_nsplit(topk));
+  return 0;
+}
+
+m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* v, const uint16_t* idx_k,
+                     int64_t row_stride, const int32_t* slot_mapping, int32_t num_tokens, uint32_t* dev_status,
+                     hipStream_t stream) {
+  m3s_status st = check_cache(cache);
+  if (st != M3S_OK) return st;
+  if (num_tokens < 0) return M3S_ERR_INVALID_ARG;
+  if (num_tokens == 0) return M3S_OK;
+  if (!slot_mapping) return M3S_ERR_INVALID_ARG;
+  if (row_stride < M3S_HEAD_DIM || (row_stride & 7)) return M3S_ERR_INVALID_ARG;
+  const uint16_t* src[3] = {k, v, idx_k};
+  uint8_t* dat[3] = {cache->k_data, cache->v_data, cache->idx_data};
+  uint8_t* scl[3] = {cache->k_scale, cache->v_scale, cache->idx_scale};
+  for (int t = 0; t < 3; ++t) {
+    if (!src[t]) continue;
+    if (!aligned16(src[t]) || !dat[t] || !scl[t]) return M3S_ERR_INVALID_ARG;
+  }
+  StoreArgs a;
+  a.format = cache->format;
+  a.k = k;
+  a.v = v;
+  a.idx = idx_k;
+  a.row_stride = row_stride;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_pages = cache->num_pages;
+  a.k_data = cache->k_data;
+  a.k_scale = cache->k_scale;
+  a.v_data = cache->v_data;
+  a.v_scale = cache->v_scale;
+  a.idx_data = cache->idx_data;
+  a.idx_scale = cache->idx_scale;
+  a.status = dev_status;
+  return from_hip(launch_store(a, stream));
+}
+
+m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
+                           int32_t* row_req, int32_t* row_len, int32_t* req_blk, uint32_t* dev_status,
+                           hipStream_t stream) {
+  if (num_reqs < 0 || num_rows < 0) return M3S_ERR_INVALID_ARG;
+  if (num_reqs > M3S_MAX_REQS || num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
+  if (!cu_q || !req_blk) return M3S_ERR_INVALID_ARG;
+  if (num_reqs > 0 && !seq_lens) return M3S_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!row_req || !row_len)) return M3S_ERR_INVALID_ARG;
+  RowsArgs a;
+  a.cu_q = cu_q;
+  a.seq_lens = seq_lens;
+  a.num_reqs = num_reqs;
+  a.num_rows = num_rows;
+  a.row_req = row_req;
+  a.row_len = row_len;
+  a.req_blk = req_blk;
+  a.status = dev_status;
+  return from_hip(launch_decode_rows(a, stream));
+}
+
+m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                          const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, const m3s_rows* rows,
+                          int32_t topk, int32_t flags, int32_t* topk_ids, void* workspace, size_t workspace_bytes,
+                          uint32_t* dev_status, hipStream_t stream) {
+  m3s_status st = check_cache(cache);
+  if (st != M3S_OK) return st;
+  if (!cache->idx_data || !cache->idx_scale) return M3S_ERR_INVALID_ARG;
+  st = check_rows(rows);
+  if (st != M3S_OK) return st;
+  st = check_table(block_table, bt_stride, max_blocks);
+  if (st != M3S_OK) return st;
+  if (topk < 1 || topk > M3S_MAX_TOPK) return M3S_ERR_UNSUPPORTED;
+  if (flags & ~(int32_t)M3S_TOPK_TIE_HIGH_ID) return M3S_ERR_INVALID_ARG;
+  if (rows->num_rows > 0) {
+    if (!q_idx || !aligned16(q_idx) || q_idx_stride < M3S_HEAD_DIM || (q_idx_stride & 7)) return M3S_ERR_INVALID_ARG;
+    if (!topk_ids) return M3S_ERR_INVALID_ARG;
+  }
+  const size_t need = index_ws_bytes(rows->num_rows, max_blocks);
+  if (workspace_bytes < need || (need > 0 && !workspace) || !aligned16(workspace)) return M3S_ERR_WORKSPACE;
+  if (rows->num_rows == 0) return M3S_OK;
+  IndexArgs a;
+  a.format = cache->format;
+  a.idx_data = cache->idx_data;
+  a.idx_scale = cache->idx_scale;
+  a.num_pages = cache->num_pages;
+  a.q_idx = q_idx;
+  a.q_stride = q_idx_stride;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.max_blocks = max_blocks;
+  a.cu_q = rows->cu_q;
+  a.row_req = rows->row_req;
+  a.row_len = rows->row_len;
+  a.req_blk = rows->req_blk;
+  a.num_reqs = rows->num_reqs;
+  a.num_rows = rows->num_rows;
+  a.topk = topk;
+  a.tie_high = (flags & M3S_TOPK_TIE_HIGH_ID) ? 1 : 0;
+  a.topk_ids = topk_ids;
+  a.ws_score = static_cast<float*>(workspace);
+  a.ws_bound = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
+  a.status = dev_status;
+  a.scan_grid = scan_grid();
+  return from_hip(launch_index_topk(a, stream));
+}
+
+m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                             int32_t num_heads, const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                             const m3s_rows* rows, const int32_t* topk_ids, int32_t topk, float sm_scale, float* out,
+                             void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
+  m3s_status st = check_cache(cache);
+  if (st != M3S_OK) return st;
+  if (!cache->k_data || !cache->k_scale || !cache->v_data || !cache->v_scale) return M3S_ERR_INVALID_ARG;
+  st = check_rows(rows);
+  if (st != M3S_OK) return st;
+  st = check_table(block_table, bt_stride, max_blocks);
+  if (st != M3S_OK) return st;
+  if (num_heads < 1 || num_heads > M3S_MAX_HEADS) return M3S_ERR_UNSUPPORTED;
+  if (topk < 1 || topk > M3S_MAX_TOPK) return M3S_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale)) return M3S_ERR_INVALID_ARG;
+  if (rows->num_rows > 0) {
+    if (!q || !aligned16(q) || (q_row_stride & 7) || (q_head_stride & 7) || q_row_stride < 0 || q_head_stride < 0)
+      return M3S_ERR_INVALID_ARG;
+    if (num_heads > 1 && q_head_stride < M3S_HEAD_DIM) return M3S_ERR_INVALID_ARG;
+    if (!topk_ids || !out) return M3S_ERR_INVALID_ARG;
+  }
+  const int32_t nsplit = attend_nsplit(topk);
+  const size_t need = attend_ws_bytes(rows->num_rows, nsplit);
+  if (workspace_bytes < need || (need > 0 && !workspace) || !aligned16(workspace)) return M3S_ERR_WORKSPACE;
+  if (rows->num_rows == 0) return M3S_OK;
+  AttendArgs a;
+  a.format = cache->format;
+  a.k_data = cache->k_data;
+  a.k_scale = cache->k_scale;
+  a.v_data = cache->v_data;
+  a.v_scale = cache->v_scale;
+  a.num_pages = cache->num_pages;
+  a.q = q;
+  a.q_row_stride = q_row_stride;
+  a.q_head_stride = q_head_stride;
+  a.num_heads = num_heads;
+  a.block_table = block_table;
+  a.bt_stride = bt_stride;
+  a.max_blocks = max_blocks;
+  a.row_req = rows->row_req;
+  a.row_len = rows->row_len;
+  a.num_rows = rows->num_rows;
+  a.topk_ids = topk_ids;
+  a.topk = topk;
+  a.nsplit = nsplit;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  const size_t po = ((size_t)rows->num_rows * nsplit * 16 * M3S_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + po) : nullptr;
+  a.status = dev_status;
+  return from_hip(launch_sparse_attend(a, stream));
+}
+
+m3s_status m3s_read_device_status(const uint32_t* dev_status, uint32_t* out, hipStream_t stream) {
+  if (!dev_status || !out) return M3S_ERR_INVALID_ARG;
+  hipError_t e = hipMemcpyAsync(out, dev_status, sizeof(uint32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Device helpers for the NVFP4 / MXFP4 decode path on gfx950 (MI355X).
+//
+// Formats ([ATOM-2744] Design / Write path and Follow-up: MXFP4 caches; see
+// include/m3s.h for the source key): e2m1 codes (bit 3 sign, 2 exponent bits
+// with bias 1, 1 mantissa bit), two per byte, element 2j in the low nibble;
+// NVFP4 scales are OCP E4M3FN bytes (one per 16 elements), MXFP4 scales are
+// E8M0 bytes (one per 32 elements).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3s {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kPage = 128;
+constexpr int kDim = 128;
+constexpr int kPayload = 64;  // bytes of e2m1 codes per token
+
+// Exact value of an OCP E4M3FN byte (the NaN byte is never produced by the store).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// Exact value of an E8M0 byte: 2^(b - 127); byte 0 is the fp32 denormal 2^-127.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+
+// e2m1 -> fp16 decode.
+//
+// gfx950's scaled conversion (v_cvt_scalef32_pk_f16_fp4) applies only the
+// exponent of its fp32 scale operand (checked on MI355X for all 16 codes x all
+// 126 positive finite E4M3 scales: a non-power-of-two scale is truncated to
+// its power of two). So an NVFP4 group is decoded with scale 1.0 and then
+// multiplied by the E4M3 scale in fp16, which is exact: code * scale has at
+// most 6 significant bits and lies in [2^-10, 2688]. An MXFP4 (E8M0) scale is
+// a power of two and goes straight into the conversion.
+
+// 8 codes of one dword (element e in bits [4e, 4e+4)) as fp16, unscaled.
+__device__ __forceinline__ f16x8 fp4x8_to_f16_unscaled(uint32_t d) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
+  f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = e[0]; r[7] = e[1];
+  return r;
+}
+
+// 8 codes times a power-of-two scale `p2` (E8M0), exact.
+__device__ __forceinline__ f16x8 fp4x8_to_f16_pow2(uint32_t d, float p2) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 0);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 1);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 2);
+  f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 3);
+  f16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = e[0]; r[7] = e[1];
+  return r;
+}
+
+// E4M3FN scale byte -> the same value in fp16 (exact: 2^-9 .. 448 are fp16 normals).
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) { return (_Float16)e4m3_to_f32(b); }
+
+// 8 codes of one dword times an E4M3 scale, as fp16 (exact).
+__device__ __forceinline__ f16x8 fp4x8_to_f16_e4m3(uint32_t d, _Float16 s) {
+  f16x8 r = fp4x8_to_f16_unscaled(d);
+  f16x8 sv = {s, s, s, s, s, s, s, s};
+  return r * sv;
+}
+
+template <int FMT>
+struct Decode;
+template <>
+struct Decode<1> {  // NVFP4: scale byte is E4M3FN
+  typedef _Float16 scale_t;
+  static __device__ __forceinline__ scale_t scale(uint32_t byte) { return e4m3_to_f16(byte); }
+  static __device__ __forceinline__ f16x8 run(uint32_t d, scale_t s) { return fp4x8_to_f16_e4m3(d, s); }
+};
+template <>
+struct Decode<2> {  // MXFP4: scale byte is E8M0
+  typedef float scale_t;
+  static __device__ __forceinline__ scale_t scale(uint32_t byte) { return e8m0_to_f32(byte); }
+  static __device__ __forceinline__ f16x8 run(uint32_t d, scale_t s) { return fp4x8_to_f16_pow2(d, s); }
+};
+
+// Scale of the 16-element (NVFP4) or 32-element (MXFP4) group as fp32.
+template <int FMT>
+__device__ __forceinline__ float scale_to_f32(uint32_t byte);
+template <>
+__device__ __forceinline__ float scale_to_f32<1>(uint32_t byte) { return e4m3_to_f32(byte); }
+template <>
+__device__ __forceinline__ float scale_to_f32<2>(uint32_t byte) { return e8m0_to_f32(byte); }
+
+// 16x16x32 MFMA. Lane l holds A[l % 16][8 * (l / 16) + e] and B[8 * (l / 16) + e][l % 16]
+// for e = 0..7; the result lane l holds D[4 * (l / 16) + v][l % 16] for v = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max_xor(float x, int lo_mask, int hi_mask) {
+  for (int m = lo_mask; m <= hi_mask; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum_xor(float x, int lo_mask, int hi_mask) {
+  for (int m = lo_mask; m <= hi_mask; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+__device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {
+  if (status) atomicOr(status, bit);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+}  // namespace m3s

@@ -1,0 +1,117 @@
+// Internal interface between the C-ABI host layer (api.cpp) and the kernel
+// translation units. Argument structs are passed by value as kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3s {
+
+// Device status bits (mirror of the M3S_DEV_* values in m3s.h).
+enum : uint32_t {
+  kDevBadSlot = 1u << 0,
+  kDevBadRows = 1u << 1,
+  kDevBadLength = 1u << 2,
+  kDevBadPage = 1u << 3,
+  kDevBadBlockId = 1u << 4,
+  kDevInexact = 1u << 5,
+  kDevBandOverflow = 1u << 6,
+};
+
+constexpr int kMaxBlocks = 8192;   // causal blocks per request
+constexpr int kMaxQLen = 16;
+constexpr int kBandCap = 1024;     // exact-rescore capacity per row
+
+struct StoreArgs {
+  int format;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* idx;
+  int64_t row_stride;
+  const int32_t* slots;
+  int32_t num_tokens;
+  int32_t num_pages;
+  uint8_t* k_data;
+  uint8_t* k_scale;
+  uint8_t* v_data;
+  uint8_t* v_scale;
+  uint8_t* idx_data;
+  uint8_t* idx_scale;
+  uint32_t* status;
+};
+
+struct RowsArgs {
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  int32_t num_reqs;
+  int32_t num_rows;
+  int32_t* row_req;
+  int32_t* row_len;
+  int32_t* req_blk;
+  uint32_t* status;
+};
+
+struct IndexArgs {
+  int format;
+  const uint8_t* idx_data;
+  const uint8_t* idx_scale;
+  int32_t num_pages;
+  const uint16_t* q_idx;
+  int64_t q_stride;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t max_blocks;
+  const int32_t* cu_q;
+  const int32_t* row_req;
+  const int32_t* row_len;
+  const int32_t* req_blk;
+  int32_t num_reqs;
+  int32_t num_rows;
+  int32_t topk;
+  int32_t tie_high;
+  int32_t* topk_ids;
+  float* ws_score;   // [num_rows, max_blocks]
+  float* ws_bound;   // [num_rows, max_blocks]
+  uint32_t* status;
+  int32_t scan_grid; // workgroups of the scan kernel
+};
+
+struct AttendArgs {
+  int format;
+  const uint8_t* k_data;
+  const uint8_t* k_scale;
+  const uint8_t* v_data;
+  const uint8_t* v_scale;
+  int32_t num_pages;
+  const uint16_t* q;
+  int64_t q_row_stride;
+  int64_t q_head_stride;
+  int32_t num_heads;
+  const int32_t* block_table;
+  int32_t bt_stride;
+  int32_t max_blocks;
+  const int32_t* row_req;
+  const int32_t* row_len;
+  int32_t num_rows;
+  const int32_t* topk_ids;
+  int32_t topk;
+  int32_t nsplit;
+  float sm_scale;
+  float* out;
+  float* part_o;   // [num_rows, nsplit, 16, 128]
+  float* part_ml;  // [num_rows, nsplit, 16, 2]
+  uint32_t* status;
+};
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+hipError_t launch_decode_rows(const RowsArgs& a, hipStream_t stream);
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
+hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);
+
+// Workspace layout helpers shared by sizing and launching.
+size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks);
+size_t attend_ws_bytes(int32_t num_rows, int32_t nsplit);
+int32_t attend_nsplit(int32_t topk);
+
+}  // namespace m3s

@@ -1,0 +1,254 @@
+/*
+ * m3s.h - C ABI of the decode hot path for block-sparse attention over
+ * NVFP4 / MXFP4 paged caches (MiniMax-M3 indexed sparse-attention layers),
+ * built for MI355X (gfx950).
+ *
+ * Four calls make one decode step, issued in this order on one stream:
+ *
+ *   m3s_store          quantize the step's new K, V and index-K rows and write
+ *                      them into the paged uint8 planes at their slots
+ *   m3s_decode_rows    map every decode / verify row to (request, causal length)
+ *   m3s_index_topk     score every causal 128-token block of every row against
+ *                      the FP4 index cache, keep each row's top-k block ids
+ *   m3s_sparse_attend  GQA softmax attention of each row over only its top-k
+ *                      blocks of the FP4 K/V cache
+ *
+ * Sources (web pages; sections named, not quoted):
+ *   [ATOM-2746]  ROCm/ATOM PR "NVFP4 sparse KV", Summary and Tests.
+ *   [ATOM-2744]  ROCm/ATOM PR "[MiniMax-M3.1] FP4 index cache and NVFP4 sparse
+ *                KV cache", Design (Kernels, Write path, Index, Decode score
+ *                grid, Attention, Fused verify top-k), Follow-up: MXFP4
+ *                caches, Tests, and the review notes on ties, ascending ids,
+ *                page size and invalid block ids.
+ *   [VLLM-64198] vllm-project/vllm PR "MXFP4 KV + indexer cache for
+ *                MiniMax-M3.1", Claims and Design.
+ *
+ * Conventions shared by every call:
+ *   - All tensor pointers are DEVICE pointers unless a comment says "host".
+ *     The caller owns every buffer; the library never allocates, frees or
+ *     synchronizes inside these calls. Every call is asynchronous on `stream`
+ *     and may be captured into a HIP graph (all counts that depend on device
+ *     data are read on the device; nothing is read back to the host).
+ *   - bf16 tensors are passed as `const uint16_t*` (raw bfloat16 bits).
+ *   - Host-side validation runs first and is synchronous. It returns
+ *     M3S_ERR_INVALID_ARG (null pointer, negative count, too-small stride) or
+ *     M3S_ERR_UNSUPPORTED (a shape the kernels do not implement) or
+ *     M3S_ERR_WORKSPACE (workspace null or smaller than m3s_workspace_bytes)
+ *     without touching the GPU. M3S_ERR_HIP reports a failed launch.
+ *   - Device-side problems (an out-of-range page or block id, a bad length)
+ *     never wrap and never fault: the kernel ORs an M3S_DEV_* bit into
+ *     `*dev_status` (one uint32 on the device, optional: may be NULL) and the
+ *     affected row produces -1 ids / zero output. The bits are sticky; the
+ *     caller clears the word.
+ *   - No C++ exception crosses this boundary.
+ *
+ * Geometry (fixed): page = sparse block = 128 tokens ([ATOM-2744] review:
+ * the block size must equal the page size), head_dim = 128, one KV head and
+ * one index head per GPU (one rank of a TP4 deployment).
+ */
+#ifndef M3S_H
+#define M3S_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define M3S_VERSION 1
+
+#define M3S_PAGE 128
+#define M3S_HEAD_DIM 128
+#define M3S_MAX_Q_LEN 16     /* rows per request (1 target + up to 15 drafts) */
+#define M3S_MAX_HEADS 16     /* query heads per KV head (G) */
+#define M3S_MAX_TOPK 64
+#define M3S_MAX_REQS 4096
+#define M3S_MAX_ROWS 65536
+#define M3S_MAX_BLOCKS 8192  /* causal blocks per request: 1,048,576 tokens */
+
+typedef int32_t m3s_status;
+enum {
+  M3S_OK = 0,
+  M3S_ERR_INVALID_ARG = 1,
+  M3S_ERR_UNSUPPORTED = 2,
+  M3S_ERR_WORKSPACE = 3,
+  M3S_ERR_HIP = 4
+};
+
+/* Cache formats ([ATOM-2746] Summary; [ATOM-2744] Follow-up: MXFP4 caches;
+ * [VLLM-64198] Claims). */
+enum {
+  M3S_FMT_NVFP4 = 1, /* e2m1 codes + one E4M3FN scale per 16 elements: 64 + 8 B per token */
+  M3S_FMT_MXFP4 = 2  /* e2m1 codes + one E8M0 scale per 32 elements:   64 + 4 B per token */
+};
+
+/* Sticky device status bits (ORed into *dev_status). */
+enum {
+  M3S_DEV_BAD_SLOT = 1u << 0,     /* store: slot >= num_pages * 128 */
+  M3S_DEV_BAD_ROWS = 1u << 1,     /* decode_rows: q_len outside [1, 16], seq_len < q_len,
+                                     cu_q not non-decreasing, or cu_q[B] > num_rows */
+  M3S_DEV_BAD_LENGTH = 1u << 2,   /* a live row needs more than max_blocks blocks */
+  M3S_DEV_BAD_PAGE = 1u << 3,     /* block table entry outside [0, num_pages) */
+  M3S_DEV_BAD_BLOCK_ID = 1u << 4, /* attend: top-k id outside the row's causal blocks */
+  M3S_DEV_INEXACT = 1u << 5,      /* index_topk: an exact rescore could not prove its
+                                     float64 sum exact (ids may then differ from exact
+                                     arithmetic in a near tie) */
+  M3S_DEV_BAND_OVERFLOW = 1u << 6 /* index_topk: more than 1024 blocks inside a row's
+                                     uncertainty band; that row fell back to the
+                                     approximate scores */
+};
+
+/* Flags of m3s_index_topk. */
+enum {
+  M3S_TOPK_TIE_HIGH_ID = 1 /* equal scores rank the higher block id first (the rule of
+                              the [ATOM-2744] review notes); default: lower id first */
+};
+
+/*
+ * One KV head's paged cache (host struct; the plane pointers are device
+ * pointers). Reading of [ATOM-2746] Summary ("k/v and k_scale/v_scale are
+ * uint8 planes") and [VLLM-64198] Claims (page = [128 x 64 B][128 x 4 B]):
+ * each tensor (K, V, index K) has a payload plane and a scale plane, page
+ * major; slot s = page * 128 + offset lives at
+ *     payload[page][offset][0..64)   byte j = code(2j) | code(2j+1) << 4
+ *     scale  [page][offset][0..SB)   SB = 8 (NVFP4) or 4 (MXFP4)
+ * page_size must be 128, head_dim 128, num_kv_heads 1.
+ */
+typedef struct m3s_cache {
+  int32_t format;       /* M3S_FMT_NVFP4 or M3S_FMT_MXFP4 */
+  int32_t num_pages;
+  int32_t page_size;    /* = 128 */
+  int32_t head_dim;     /* = 128 */
+  int32_t num_kv_heads; /* = 1 */
+  uint8_t* k_data;
+  uint8_t* k_scale;
+  uint8_t* v_data;
+  uint8_t* v_scale;
+  uint8_t* idx_data;
+  uint8_t* idx_scale;
+} m3s_cache;
+
+/*
+ * The row map of one step (host struct of device pointers), filled by
+ * m3s_decode_rows and shared by m3s_index_topk and m3s_sparse_attend
+ * ([ATOM-2744] Design, Attention: one decode_rows launch, shared by the
+ * attention and the fused top-k).
+ */
+typedef struct m3s_rows {
+  const int32_t* cu_q;    /* [num_reqs + 1] first row of each request (input of decode_rows) */
+  const int32_t* row_req; /* [num_rows] request of each row, -1 for a pad row */
+  const int32_t* row_len; /* [num_rows] causal length of each row, 0 for a pad row */
+  const int32_t* req_blk; /* [num_reqs + 1] exclusive prefix sum of ceil(seq_len / 128) */
+  int32_t num_reqs;
+  int32_t num_rows;       /* padded row count (>= cu_q[num_reqs]) */
+} m3s_rows;
+
+/*
+ * m3s_store - [ATOM-2744] Write path: per 16 elements scale = e4m3(amax / 6),
+ * codes rounded half to even and saturating at 6 (NVFP4); [ATOM-2744]
+ * Follow-up: MXFP4 caches: one E8M0 scale per 32 elements (MXFP4, OCP MX v1.0
+ * scale rule 2^(floor(log2 amax) - 2)). Rows with slot_mapping[t] < 0 are pad
+ * rows and are left unwritten ([ATOM-2744] Tests).
+ *
+ *   k, v, idx_k   bf16 [num_tokens, row_stride] (the first 128 elements of each
+ *                 row are used); any of the three may be NULL to skip it.
+ *   row_stride    elements between consecutive rows (>= 128).
+ *   slot_mapping  int32 [num_tokens]; slot = page * 128 + offset.
+ * A slot >= num_pages * 128 sets M3S_DEV_BAD_SLOT and is skipped.
+ * One launch covers all three tensors. NaN / Inf inputs are outside the format.
+ */
+m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* v,
+                     const uint16_t* idx_k, int64_t row_stride, const int32_t* slot_mapping,
+                     int32_t num_tokens, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * m3s_decode_rows - [ATOM-2746] Summary, Attention: one launch builds each
+ * decode row's (request, causal length) on the device. Row r in
+ * [cu_q[b], cu_q[b+1]) gets row_req = b and
+ *     row_len = seq_lens[b] - q_len_b + 1 + (r - cu_q[b]),  q_len_b = cu_q[b+1] - cu_q[b]
+ * (seq_lens include the step's own rows). Rows r >= cu_q[num_reqs] are pad
+ * rows: (-1, 0). req_blk[b] = sum over b' < b of ceil(seq_lens[b'] / 128).
+ *
+ *   cu_q       int32 [num_reqs + 1], seq_lens int32 [num_reqs]
+ *   row_req, row_len  int32 [num_rows] (outputs), req_blk int32 [num_reqs + 1] (output)
+ * A request with q_len outside [1, 16] or seq_len < q_len sets M3S_DEV_BAD_ROWS
+ * and its rows become pad rows (its block count is 0).
+ */
+m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs,
+                           int32_t num_rows, int32_t* row_req, int32_t* row_len,
+                           int32_t* req_blk, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * m3s_index_topk - [ATOM-2744] Design, Index and Decode score grid, and Fused
+ * verify top-k: score every causal 128-token block of every row against the
+ * FP4 index cache (reached through the block table) and keep the top-k.
+ *   score(row, j) = max over tokens t of block j with t < row_len of
+ *                   sum_d q_idx[row][d] * dequant(idx)[t][d]
+ * ids are the k best blocks by (score desc, id asc; id desc with
+ * M3S_TOPK_TIE_HIGH_ID), emitted ASCENDING, padded with -1 when the row has
+ * fewer than k causal blocks. The selection equals the one exact arithmetic
+ * makes: the scan computes fp32 scores with a rigorous error bound and
+ * rescores, in exact float64, every block whose rank the bound leaves open.
+ *
+ *   q_idx        bf16 [num_rows, q_idx_stride] (first 128 used)
+ *   block_table  int32 [num_reqs, bt_stride]; block j of request b lives on
+ *                page block_table[b * bt_stride + j]
+ *   max_blocks   upper bound of ceil(row_len / 128) over rows (<= bt_stride)
+ *   topk         in [1, 64]
+ *   topk_ids     int32 [num_rows, topk] (output); pad rows get -1
+ *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_INDEX_TOPK, ...)
+ */
+m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                          const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                          const m3s_rows* rows, int32_t topk, int32_t flags, int32_t* topk_ids,
+                          void* workspace, size_t workspace_bytes, uint32_t* dev_status,
+                          hipStream_t stream);
+
+/*
+ * m3s_sparse_attend - [ATOM-2746] Summary, Attention: block-sparse attention
+ * addressed by the top-k block ids and the request block table. For each
+ * row and query head h < num_heads (all heads share the one KV head):
+ *   out[row][h] = sum_t p_t * dequant(V)[t],  p = softmax_t(sm_scale * q[row][h] . dequant(K)[t])
+ * over the tokens t < row_len of the row's selected blocks. ids < 0 are
+ * skipped; an id outside [0, ceil(row_len/128)) or a page outside
+ * [0, num_pages) sets a status bit and is skipped. A row with no valid token
+ * (pad rows included) outputs zeros. ids must be distinct.
+ *
+ *   q            bf16, element (row, h, d) at q[row * q_row_stride + h * q_head_stride + d]
+ *   num_heads    G in [1, 16]
+ *   topk_ids     int32 [num_rows, topk]
+ *   out          fp32 [num_rows, num_heads, 128], contiguous
+ *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_SPARSE_ATTEND, ...)
+ * Computation: K and V are decoded exactly (bf16 / fp16), QK^T on bf16 MFMA
+ * with fp32 accumulation, online softmax in fp32, PV on fp16 MFMA; split-K
+ * partials are merged by a combine pass.
+ */
+m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t q_row_stride,
+                             int64_t q_head_stride, int32_t num_heads,
+                             const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                             const m3s_rows* rows, const int32_t* topk_ids, int32_t topk,
+                             float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                             uint32_t* dev_status, hipStream_t stream);
+
+/* Workspace sizing (host only, pure). */
+enum { M3S_OP_INDEX_TOPK = 1, M3S_OP_SPARSE_ATTEND = 2 };
+size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32_t max_blocks,
+                           int32_t topk, int32_t num_heads);
+
+/* Copies *dev_status to host memory `*out` (host pointer) and synchronizes `stream`. */
+m3s_status m3s_read_device_status(const uint32_t* dev_status, uint32_t* out, hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* m3s_status_string(m3s_status status);
+
+/* M3S_VERSION of the built library. */
+int32_t m3s_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* M3S_H */

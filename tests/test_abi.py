@@ -1,0 +1,160 @@
+"""The C-ABI library loads on a CPU-only host, exports every symbol include/m3s.h
+declares, and its host-side validation rejects bad arguments without touching
+the GPU (every call below returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_decode_nvfp4_amd as m3s
+from block_sparse_decode_nvfp4_amd import _build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m3s.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(m3s.LIB_PATH):
+        _build.build()
+    return m3s.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(m3s_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = declared_functions()
+    for n in ("m3s_store", "m3s_decode_rows", "m3s_index_topk", "m3s_sparse_attend"):
+        assert n in names
+    assert set(names) == set(m3s.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert m3s.m3s_version() == 1
+    for s in range(5):
+        assert m3s.m3s_status_string(s)
+    assert m3s.m3s_status_string(99) == "unknown status"
+
+
+def _cache(fmt=1, pages=4, page=128, dim=128, heads=1, ptr=4096):
+    return m3s.m3s_cache(fmt, pages, page, dim, heads, ptr, ptr, ptr, ptr, ptr, ptr)
+
+
+def _rows(nreq=1, nrows=1, ptr=4096):
+    return m3s.m3s_rows(ptr, ptr, ptr, ptr, nreq, nrows)
+
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first or the call is not made
+
+
+def test_store_validation(lib):
+    c = _cache()
+    E = m3s
+    st = lambda cache, k=FAKE, stride=128, slots=FAKE, T=4: lib.m3s_store(
+        ctypes.byref(cache) if cache is not None else None, k, k, k, stride, slots, T, None, None)
+    assert st(None) == E.ERR_INVALID_ARG
+    assert st(_cache(fmt=3)) == E.ERR_UNSUPPORTED
+    assert st(_cache(page=256)) == E.ERR_UNSUPPORTED            # 256-token pages are refused
+    assert st(_cache(dim=64)) == E.ERR_UNSUPPORTED
+    assert st(_cache(heads=2)) == E.ERR_UNSUPPORTED
+    assert st(_cache(pages=-1)) == E.ERR_INVALID_ARG
+    assert st(c, T=-1) == E.ERR_INVALID_ARG
+    assert st(c, T=0) == E.OK                                   # nothing to do, no launch
+    assert st(c, slots=None) == E.ERR_INVALID_ARG
+    assert st(c, stride=64) == E.ERR_INVALID_ARG
+    assert st(c, stride=130) == E.ERR_INVALID_ARG               # rows must stay 16 B aligned
+    assert st(c, k=ctypes.c_void_p(4098)) == E.ERR_INVALID_ARG  # misaligned source
+    c2 = _cache()
+    c2.v_scale = None
+    assert st(c2) == E.ERR_INVALID_ARG
+
+
+def test_decode_rows_validation(lib):
+    f = lambda cu=FAKE, seq=FAKE, B=1, R=1, rr=FAKE, rl=FAKE, rb=FAKE: lib.m3s_decode_rows(
+        cu, seq, B, R, rr, rl, rb, None, None)
+    assert f(B=-1) == m3s.ERR_INVALID_ARG
+    assert f(R=-1) == m3s.ERR_INVALID_ARG
+    assert f(B=4097) == m3s.ERR_UNSUPPORTED
+    assert f(R=65537) == m3s.ERR_UNSUPPORTED
+    assert f(cu=None) == m3s.ERR_INVALID_ARG
+    assert f(seq=None) == m3s.ERR_INVALID_ARG
+    assert f(rr=None) == m3s.ERR_INVALID_ARG
+    assert f(rb=None) == m3s.ERR_INVALID_ARG
+
+
+def _topk(lib, cache=None, q=FAKE, qs=128, bt=FAKE, bts=16, mb=16, rows=None, k=4, flags=0, ids=FAKE,
+          ws=FAKE, wsb=1 << 30):
+    cache = _cache() if cache is None else cache
+    rows = _rows() if rows is None else rows
+    return lib.m3s_index_topk(ctypes.byref(cache), q, qs, bt, bts, mb, ctypes.byref(rows), k, flags, ids,
+                              ws, wsb, None, None)
+
+
+def test_index_topk_validation(lib):
+    E = m3s
+    assert _topk(lib, cache=_cache(page=64)) == E.ERR_UNSUPPORTED
+    assert _topk(lib, k=0) == E.ERR_UNSUPPORTED
+    assert _topk(lib, k=65) == E.ERR_UNSUPPORTED
+    assert _topk(lib, flags=2) == E.ERR_INVALID_ARG
+    assert _topk(lib, mb=0) == E.ERR_INVALID_ARG
+    assert _topk(lib, bts=8, mb=16) == E.ERR_INVALID_ARG
+    assert _topk(lib, bts=9000, mb=8193) == E.ERR_UNSUPPORTED
+    assert _topk(lib, bt=None) == E.ERR_INVALID_ARG
+    assert _topk(lib, q=None) == E.ERR_INVALID_ARG
+    assert _topk(lib, qs=100) == E.ERR_INVALID_ARG
+    assert _topk(lib, ids=None) == E.ERR_INVALID_ARG
+    assert _topk(lib, rows=_rows(nreq=-1)) == E.ERR_INVALID_ARG
+    assert _topk(lib, rows=_rows(nreq=5000)) == E.ERR_UNSUPPORTED
+    need = m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 1, 1, 16, 4, 1)
+    assert need > 0
+    assert _topk(lib, wsb=need - 1) == E.ERR_WORKSPACE
+    assert _topk(lib, ws=None) == E.ERR_WORKSPACE
+    assert _topk(lib, rows=_rows(nrows=0)) == E.OK              # no rows: nothing launched
+
+
+def _attend(lib, cache=None, q=FAKE, qrs=2048, qhs=128, G=16, bt=FAKE, bts=16, mb=16, rows=None, ids=FAKE,
+            k=16, scale=1.0, out=FAKE, ws=FAKE, wsb=1 << 30):
+    cache = _cache() if cache is None else cache
+    rows = _rows() if rows is None else rows
+    return lib.m3s_sparse_attend(ctypes.byref(cache), q, qrs, qhs, G, bt, bts, mb, ctypes.byref(rows), ids, k,
+                                 scale, out, ws, wsb, None, None)
+
+
+def test_sparse_attend_validation(lib):
+    E = m3s
+    assert _attend(lib, G=0) == E.ERR_UNSUPPORTED
+    assert _attend(lib, G=17) == E.ERR_UNSUPPORTED
+    assert _attend(lib, k=65) == E.ERR_UNSUPPORTED
+    assert _attend(lib, scale=float("nan")) == E.ERR_INVALID_ARG
+    assert _attend(lib, qhs=64) == E.ERR_INVALID_ARG
+    assert _attend(lib, qrs=2050) == E.ERR_INVALID_ARG
+    assert _attend(lib, out=None) == E.ERR_INVALID_ARG
+    assert _attend(lib, ids=None) == E.ERR_INVALID_ARG
+    c = _cache()
+    c.k_scale = None
+    assert _attend(lib, cache=c) == E.ERR_INVALID_ARG
+    need = m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 1, 1, 16, 16, 16)
+    assert need > 0
+    assert _attend(lib, wsb=need - 1) == E.ERR_WORKSPACE
+    # four or fewer blocks fit one split: no workspace needed
+    assert m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 1, 1, 16, 4, 16) == 0
+    assert _attend(lib, rows=_rows(nrows=0)) == E.OK
+
+
+def test_workspace_sizes_scale_with_shape(lib):
+    a = m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 64, 8, 1172, 16, 16)
+    assert a >= 2 * 64 * 1172 * 4
+    b = m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 64, 8, 1172, 16, 16)
+    assert b >= 64 * 4 * 16 * 128 * 4
+    assert m3s.m3s_workspace_bytes(99, 1, 1, 1, 1, 1) == 0
+    assert m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 1, 1, 1, 0, 1) == 0

@@ -1,0 +1,55 @@
+"""The full step on every workload configuration, in the launch configuration the bench
+times: ids bit-exact and attention within 5e-3 of the oracle on sampled requests (all of
+their rows), stored planes bit-exact on those requests' pages."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as F
+from tests.stepcase import max_rel_err, oracle_requests, run_gpu_step, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = 5e-3
+
+# requests the oracle recomputes (whole requests: all their rows)
+SAMPLES = {0: [0], 1: [0, 5], 2: [0, 3], 3: [7, 31], 4: [2, 7]}
+
+
+@pytest.mark.parametrize("ci", [0, 1, 2, 3, 4])
+def test_config_full_step(gpu, ci):
+    cfg = W.config(ci)
+    step = run_gpu_step(gpu, cfg, DEV)
+    assert step.status == 0, hex(step.status)
+    lay = step.case.layout
+    reqs = SAMPLES[ci]
+    say(f"[config {cfg.name}] oracle on requests {reqs}")
+    ids, outs, rr, rl = oracle_requests(step, cfg.fmt, cfg.topk, cfg.sm_scale, reqs)
+    got_ids = step.ids.cpu().numpy()
+    got = step.out.cpu().double().numpy()
+    assert np.array_equal(step.rows.row_req.cpu().numpy(), rr)
+    assert np.array_equal(step.rows.row_len.cpu().numpy(), rl)
+    worst = 0.0
+    for r in ids:
+        assert got_ids[r].tolist() == ids[r].tolist(), (r, got_ids[r].tolist(), ids[r].tolist())
+        worst = max(worst, max_rel_err(got[r], outs[r]))
+    say(f"[config {cfg.name}] ids equal on {len(ids)} rows, max rel err {worst:.2e}")
+    assert worst <= TOL
+    # stored planes of the sampled requests (index plane: every page; K/V: the new rows' pages)
+    sb = 8 if cfg.fmt == "nvfp4" else 4
+    for b in reqs:
+        lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
+        slots = W.all_slots(lay)[lo:hi].astype(np.int64)
+        wp, ws = F.quantize(cfg.fmt, W.bf16_bits(step.case.idx[lo:hi]))
+        p, s = step.cache.planes["idx"]
+        p = p.view(-1, 64)[torch.as_tensor(slots, device=DEV)].cpu().numpy()
+        s = s.view(-1, sb)[torch.as_tensor(slots, device=DEV)].cpu().numpy()
+        assert np.array_equal(p, wp) and np.array_equal(s, ws), b
+    new = lay.new_tokens
+    for name in ("k", "v"):
+        wp, ws = F.quantize(cfg.fmt, W.bf16_bits(getattr(step.case, name)[torch.as_tensor(new, device=DEV)]))
+        p, s = step.cache.planes[name]
+        sl = torch.as_tensor(lay.new_slots.astype(np.int64), device=DEV)
+        assert np.array_equal(p.view(-1, 64)[sl].cpu().numpy(), wp)
+        assert np.array_equal(s.view(-1, sb)[sl].cpu().numpy(), ws)

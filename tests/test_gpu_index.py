@@ -1,0 +1,117 @@
+"""m3s_index_topk parity: top-k ids bit-exact against the oracle (small sizes, every row)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.stepcase import oracle_requests, run_gpu_step, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+CFG0 = W.config(0)
+
+
+def _check_all(gpu, step, fmt, topk, tie_high=False, q_idx_bits=None):
+    lay = step.case.layout
+    B = len(lay.seq_lens)
+    ids, _, rr, _ = oracle_requests(step, fmt, topk, 1.0, range(B), tie_high, q_idx_bits)
+    got = step.ids.cpu().numpy()
+    for r, want in ids.items():
+        assert got[r].tolist() == want.tolist(), (r, got[r].tolist(), want.tolist())
+    for r in range(len(rr)):
+        if rr[r] < 0:
+            assert np.all(got[r] == -1)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("topk", [1, 4, 16, 64])
+def test_index_small_ragged(gpu, fmt, topk):
+    seq = [2048, 5000, 300, 129, 128, 127, 17, 9000]
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=seq, q_len=3, G=4, topk=topk, fmt=fmt)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, fmt, topk)
+
+
+@pytest.mark.parametrize("q_len", [1, 8, 16])
+def test_index_q_len_and_pad_rows(gpu, q_len):
+    seq = [4000, 1500, 260]
+    R = len(seq) * q_len + 5
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=seq, q_len=q_len, G=2, topk=8, num_rows=R)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, "nvfp4", 8)
+    assert np.all(step.ids.cpu().numpy()[len(seq) * q_len:] == -1)
+
+
+@pytest.mark.parametrize("tie_high", [False, True])
+def test_index_zero_query_ties(gpu, tie_high):
+    """Zero queries: every score is 0; ties go to the lower (or higher) ids. Three and four
+    requests, as in the ATOM tie test."""
+    for nreq in (3, 4):
+        seq = [3000] * nreq
+        case = W.make_case(CFG0, DEV, seq_lens=seq, q_len=2, G=2)
+        case.q_idx = torch.zeros_like(case.q_idx)
+        step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case, flags=1 if tie_high else 0)
+        assert step.status == 0
+        nb = (3000 + 127) // 128
+        want = list(range(nb - 16, nb)) if tie_high else list(range(16))
+        assert all(row == want for row in step.ids.cpu().numpy().tolist())
+
+
+def test_index_equal_blocks_need_exact_rescore(gpu):
+    """Every page holds the same tokens, so every block ties exactly but the fp32 error
+    bound is non-zero: the band covers all blocks and the exact rescore must order them
+    by id."""
+    case = W.make_case(CFG0, DEV, seq_lens=[128 * 40, 128 * 33 + 5], q_len=2, G=2)
+    lay = case.layout
+    for b in range(2):
+        lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
+        n = hi - lo
+        base = case.idx[lo: lo + 128].clone()
+        reps = (n + 127) // 128
+        case.idx[lo:hi] = base.repeat(reps, 1)[:n]
+    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, "nvfp4", 16)
+
+
+def test_index_near_ties_are_decided_exactly(gpu):
+    """Blocks that differ from block 0 by a single tiny element: exact scores differ far
+    below the fp32 error bound, so the selection is decided by the float64 rescore."""
+    case = W.make_case(CFG0, DEV, seq_lens=[128 * 64], q_len=4, G=2)
+    n = 128 * 64
+    base = case.idx[:128].clone()
+    idx = base.repeat(64, 1)
+    g = torch.Generator(device="cpu").manual_seed(5)
+    # perturb one element of one token per block by a tiny bf16 amount
+    for j in range(64):
+        t = j * 128 + int(torch.randint(0, 128, (1,), generator=g))
+        d = int(torch.randint(0, 128, (1,), generator=g))
+        idx[t, d] = (idx[t, d].float() * (1 + 2.0 ** -7 * int(torch.randint(-2, 3, (1,), generator=g)))).to(torch.bfloat16)
+    case.idx[:n] = idx
+    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, "nvfp4", 16)
+
+
+def test_index_fewer_blocks_than_k(gpu):
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=[100, 300, 1000], q_len=2, G=2, topk=16)
+    got = step.ids.cpu().numpy()
+    assert got[0].tolist() == [0] + [-1] * 15
+    assert got[2].tolist() == [0, 1, 2] + [-1] * 13
+    assert got[4].tolist() == list(range(8)) + [-1] * 8
+
+
+def test_index_bad_page_is_flagged(gpu):
+    """A block-table entry outside [0, num_pages) is never read: the block scores -inf and
+    the device status says why."""
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=[3000], q_len=1, G=2, topk=4)
+    assert step.status == 0
+    lay = step.case.layout
+    bad = lay.block_table.copy()
+    bad[0, 5] = lay.num_pages + 7
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids = gpu.m3s_index_topk(step.cache, step.case.q_idx, torch.as_tensor(bad, device=DEV), lay.max_blocks,
+                             step.rows, 4, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & gpu.DEV_BITS["BAD_PAGE"]
+    assert 5 not in ids.cpu().numpy()[0].tolist()
