@@ -197,20 +197,14 @@ def main():
         log(f"[bench] device status {st:#x}")
         sys.exit(3)
 
-    # ---- graphs: one per layer, with HIP event records between the stages
+    # ---- graphs: one per layer (the whole step)
     side = torch.cuda.Stream()
-    graphs, evsets, staged = [], [], True
+    graphs = []
     for c in caches:
         g = torch.cuda.CUDAGraph()
-        evs = None
-        try:
-            evs = [torch.cuda.Event(enable_timing=True, external=True) for _ in range(5)]
-        except TypeError:
-            staged = False
         with torch.cuda.graph(g, stream=side):
-            run_step(c, evs if staged else None)
+            run_step(c)
         graphs.append(g)
-        evsets.append(evs)
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; {NL} layers x {lay.num_pages} pages; "
         f"rows {R}, G {G}, top-k {cfg.topk}")
@@ -232,19 +226,23 @@ def main():
     ms_per_step = ms_total / args.steps
     st = int(status.item())
 
-    # ---- per-stage HIP-event times (graph replays, one layer each, synchronized)
-    stage_ms = None
-    if staged and evsets[0] is not None:
-        acc = np.zeros(4)
-        n = 0
-        for i in range(args.stage_reps):
-            L = (i + 3) % NL
-            graphs[L].replay()
-            torch.cuda.synchronize()
-            evs = evsets[L]
-            acc += [evs[j].elapsed_time(evs[j + 1]) for j in range(4)]
+    # ---- per-stage HIP-event times. Events cannot be recorded inside a captured graph on
+    # ROCm, so the stages are launched eagerly on the same stream with events between
+    # them; a GPU spin first lets every launch queue up before the GPU reaches it, so no
+    # host launch gap lands between two events.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
+    acc = np.zeros(4)
+    n = 0
+    for rep in range(max(1, args.stage_reps // 10)):
+        torch.cuda._sleep(3_000_000)
+        for i in range(10):
+            run_step(caches[(rep * 10 + i + 1) % NL], evs[i])
+        torch.cuda.synchronize()
+        for i in range(10):
+            acc += [evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
             n += 1
-        stage_ms = (acc / n).tolist()
+    stage_ms = (acc / n).tolist()
+    st = st | int(status.item())
 
     ids_np = ids.cpu().numpy()
     by = step_bytes(cfg, lay, ids_np, G)

@@ -6,7 +6,7 @@
 
 #include <hip/hip_runtime_api.h>
 
-#include "../../include/m3s.h"
+#include "m3s.h"
 #include "launch.hpp"
 
 using namespace m3s;
@@ -47,7 +47,7 @@ int scan_grid() {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  cached = 8 * cus;
+  cached = 2 * cus;  // the scan kernel keeps 2 workgroups (8 waves) resident per CU
   return cached;
 }
 

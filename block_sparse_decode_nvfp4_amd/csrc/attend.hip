@@ -125,8 +125,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, 64));
+    mx = lane_max<1, 64>(mx);
     int P = 0;
     if (mx) {
       const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
@@ -168,8 +167,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
     float mx_l = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) mx_l = fmaxf(mx_l, fmaxf(fmaxf(st[i][0], st[i][1]), fmaxf(st[i][2], st[i][3])));
-    mx_l = fmaxf(mx_l, __shfl_xor(mx_l, 16, 64));
-    mx_l = fmaxf(mx_l, __shfl_xor(mx_l, 32, 64));
+    mx_l = lane_fmax<16, 64>(mx_l);
     m_run = mx_l;  // finite: the block has at least one causal token
     float lsum = 0.f;
 #pragma unroll
@@ -180,8 +178,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
         st[i][v] = p;
         lsum += p;
       }
-    lsum += __shfl_xor(lsum, 16, 64);
-    lsum += __shfl_xor(lsum, 32, 64);
+    lsum = lane_sum<16, 64>(lsum);
     l_run = lsum;
 
     // ---- O += P V, 32 tokens (tiles 2c, 2c+1) per step

@@ -113,13 +113,73 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max_xor(float x, int lo_mask, int hi_mask) {
-  for (int m = lo_mask; m <= hi_mask; m <<= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-  return x;
+// Cross-lane exchange with lane ^ M without the LDS crossbar: DPP quad_perm for
+// M = 1, 2; two DPP mirrors for M = 4 (half_mirror then quad xor 3) and M = 8
+// (row_mirror then half_mirror); gfx950's permlane16 / permlane32 swaps for
+// M = 16, 32 (the swap returns the even and the odd row halves; the partner is
+// the other half). Each pattern was checked lane by lane on MI355X.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wave_sum_xor(float x, int lo_mask, int hi_mask) {
-  for (int m = lo_mask; m <= hi_mask; m <<= 1) x += __shfl_xor(x, m, 64);
-  return x;
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+  if constexpr (M == 1) return dpp_mov<0xB1>(x);
+  else if constexpr (M == 2) return dpp_mov<0x4E>(x);
+  else if constexpr (M == 4) return dpp_mov<0x1B>(dpp_mov<0x141>(x));
+  else if constexpr (M == 8) return dpp_mov<0x141>(dpp_mov<0x140>(x));
+  else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (threadIdx.x & 16) ? r[0] : r[1];
+  } else {
+    static_assert(M == 32, "lane_xor: M must be a power of two below 64");
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (threadIdx.x & 32) ? r[0] : r[1];
+  }
+}
+template <int M>
+__device__ __forceinline__ float lane_xor(float x) {
+  return __uint_as_float(lane_xor_u32<M>(__float_as_uint(x)));
+}
+template <int M>
+__device__ __forceinline__ int lane_xor(int x) {
+  return (int)lane_xor_u32<M>((uint32_t)x);
+}
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+  return lane_xor_u32<M>(x);
+}
+template <int M>
+__device__ __forceinline__ uint64_t lane_xor(uint64_t x) {
+  return ((uint64_t)lane_xor_u32<M>((uint32_t)(x >> 32)) << 32) | lane_xor_u32<M>((uint32_t)x);
+}
+template <int M>
+__device__ __forceinline__ double lane_xor(double x) {
+  return __longlong_as_double((long long)lane_xor<M>((uint64_t)__double_as_longlong(x)));
+}
+
+// Butterfly reductions over the lanes whose index differs in bits LO..HI-1
+// (e.g. <1, 16>: the 16 lanes of a row; <16, 64>: the four rows; <1, 64>: all).
+template <int LO, int HI, typename T, typename F>
+__device__ __forceinline__ T lane_reduce(T x, F op) {
+  if constexpr (LO < HI) {
+    x = op(x, lane_xor<LO>(x));
+    return lane_reduce<LO * 2, HI>(x, op);
+  } else {
+    return x;
+  }
+}
+template <int LO, int HI, typename T>
+__device__ __forceinline__ T lane_max(T x) {
+  return lane_reduce<LO, HI>(x, [](T a, T b) { return a > b ? a : b; });
+}
+template <int LO, int HI>
+__device__ __forceinline__ float lane_fmax(float x) {
+  return lane_reduce<LO, HI>(x, [](float a, float b) { return __builtin_fmaxf(a, b); });
+}
+template <int LO, int HI, typename T>
+__device__ __forceinline__ T lane_sum(T x) {
+  return lane_reduce<LO, HI>(x, [](T a, T b) { return a + b; });
 }
 
 __device__ __forceinline__ void set_status(uint32_t* status, uint32_t bit) {

@@ -41,6 +41,7 @@
 namespace m3s {
 
 constexpr float kAccRel = 0x1p-15f;
+constexpr int M3S_MAX_REQS_INTERNAL = 4096;
 
 __device__ __forceinline__ uint32_t ord_f32(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);  // -0.0 -> +0.0
@@ -59,142 +60,213 @@ __device__ __forceinline__ int bf16_floor_log2(uint32_t m) {
 // ---------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------
+// One 128-token page of the index cache, as the lanes of a wave hold it:
+// lane (G, t) has token 16 i + t, dims [32 G, 32 G + 32) of tile i.
+struct PageBuf {
+  u32x4 kr[8];
+  uint32_t ks[8];
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_page(PageBuf& p, const IndexArgs& a, int page, int n, int G) {
+  constexpr int SB = FMT == 1 ? 8 : 4;
+  const uint8_t* pay = a.idx_data + (int64_t)page * (kPage * kPayload);
+  const uint8_t* scb = a.idx_scale + (int64_t)page * (kPage * SB);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p.kr[i] = *reinterpret_cast<const u32x4*>(pay + (16 * i + n) * kPayload + 16 * G);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (FMT == 1) p.ks[i] = *reinterpret_cast<const uint16_t*>(scb + (16 * i + n) * SB + 2 * G);
+    else p.ks[i] = scb[(16 * i + n) * SB + G];
+  }
+}
+
+// Per-request query state of a wave (rows r0 .. r0 + ql - 1 of request b).
+struct QueryTile {
+  f16x8 op[4];
+  float qs0, qs1, qe0, qe1, unscale;
+  int b, r0, ql, len_n, min_len;
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int n, int G) {
+  q.b = b;
+  q.r0 = a.cu_q[b];
+  q.ql = a.cu_q[b + 1] - q.r0;
+  q.min_len = a.row_len[q.r0];
+  q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
+  u32x4 raw[4] = {};
+  if (n < q.ql) {
+    const uint16_t* qp = a.q_idx + (int64_t)(q.r0 + n) * a.q_stride + 32 * G;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+  }
+  uint32_t mx = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = max(mx, max(raw[s][w] & 0x7FFFu, (raw[s][w] >> 16) & 0x7FFFu));
+  mx = lane_max<16, 64>(mx);
+  int P = mx ? 13 - bf16_floor_log2(mx) : 0;
+  P = P > 64 ? 64 : (P < -64 ? -64 : P);
+  q.unscale = __builtin_ldexpf(1.0f, -P);
+  q.qs0 = q.qs1 = q.qe0 = q.qe1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
+      const float x = __builtin_ldexpf(bf16_bits_to_f32(bits), P);
+      const _Float16 h = (_Float16)x;
+      const float err = fabsf(x - (float)h);
+      q.op[s][e] = h;
+      if (FMT == 1 && s >= 2) { q.qs1 += fabsf((float)h); q.qe1 += err; }
+      else { q.qs0 += fabsf((float)h); q.qe0 += err; }
+    }
+  }
+}
+
+// Score one page against the request's rows; write the fp32 score and error bound.
+template <int FMT>
+__device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q, const IndexArgs& a, int j, int n,
+                                           int G) {
+  const bool need_mask = (j + 1) * kPage > q.min_len;
+  float run = -INFINITY;
+  f16x2 smx = {(_Float16)0.f, (_Float16)0.f};  // largest scale of groups (2G, 2G+1) seen by this lane
+  float smx_mx = 0.f;                          // MXFP4: largest E8M0 scale of group G
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (FMT == 1) {
+      // both E4M3 scales of the lane's two groups in one conversion (OCP E4M3FN, exact)
+      const auto sf = __builtin_amdgcn_cvt_pk_f32_fp8((int)p.ks[i], false);
+      const f16x2 sc = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[1]));
+      smx = __builtin_elementwise_max(smx, sc);
+      const f16x8 s0 = {sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+      const f16x8 s1 = {sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][0]) * s0, q.op[0], acc);
+      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][1]) * s0, q.op[1], acc);
+      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][2]) * s1, q.op[2], acc);
+      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][3]) * s1, q.op[3], acc);
+    } else {
+      const float s = e8m0_to_f32(p.ks[i]);
+      smx_mx = fmaxf(smx_mx, s);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc = mfma_f16(fp4x8_to_f16_pow2(p.kr[i][t], s), q.op[t], acc);
+    }
+    if (need_mask) {
+      const int t0 = j * kPage + 16 * i + 4 * G;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        if (t0 + v >= q.len_n) acc[v] = -INFINITY;
+    }
+    run = __builtin_fmaxf(__builtin_fmaxf(run, acc[0]), acc[1]);
+    run = __builtin_fmaxf(__builtin_fmaxf(run, acc[2]), acc[3]);
+  }
+  run = lane_fmax<16, 64>(run);
+  float part;
+  if (FMT == 1) {
+    const float m0 = lane_fmax<1, 16>((float)smx[0]), m1 = lane_fmax<1, 16>((float)smx[1]);
+    part = 6.0f * (m0 * (kAccRel * q.qs0 + q.qe0) + m1 * (kAccRel * q.qs1 + q.qe1));
+  } else {
+    const float m0 = lane_fmax<1, 16>(smx_mx);
+    part = 6.0f * m0 * (kAccRel * q.qs0 + q.qe0);
+  }
+  part = lane_sum<16, 64>(part);
+  if (G == 0 && n < q.ql) {
+    const int64_t o = (int64_t)(q.r0 + n) * a.max_blocks + j;
+    a.ws_score[o] = run * q.unscale;
+    a.ws_bound[o] = part * q.unscale * (1.0f + 0x1p-10f);
+  }
+}
+
+// Streaming scan. The (request, block) units of all requests form one flat list
+// (block fastest); wave w of the grid takes the contiguous slice
+// [w * N / W, (w + 1) * N / W). The block-table entries of a wave's units are
+// fetched lane-parallel up front, and each page's loads are issued one unit
+// ahead of its scoring, so every wave keeps about two pages in flight.
 template <int FMT>
 __global__ __launch_bounds__(256) void index_scan_kernel(IndexArgs a) {
-  constexpr int SB = FMT == 1 ? 8 : 4;  // scale bytes per token
-  typedef Decode<FMT> Dec;
+  __shared__ int s_blk[M3S_MAX_REQS_INTERNAL + 1];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int n = lane & 15;   // A operand: token of the tile; B operand / result: query row
-  const int G = lane >> 4;   // lane group: dims [32G, 32G + 32)
-  __shared__ int s_b0;
-
-  const int64_t total = a.req_blk[a.num_reqs];
-  const int64_t u_begin = total * blockIdx.x / gridDim.x;
-  const int64_t u_end = total * (blockIdx.x + 1) / gridDim.x;
-  if (u_begin >= u_end) return;  // uniform over the workgroup
-
-  if (threadIdx.x == 0) s_b0 = 0;
+  const int n = lane & 15, G = lane >> 4;
+  const int B = a.num_reqs;
+  for (int i = threadIdx.x; i <= B; i += 256) s_blk[i] = a.req_blk[i];
   __syncthreads();
-  for (int b = threadIdx.x; b < a.num_reqs; b += 256)
-    if (a.req_blk[b] <= u_begin && u_begin < a.req_blk[b + 1]) s_b0 = b;
-  __syncthreads();
-  int b = s_b0;
+  const int64_t total = s_blk[B];
+  const int64_t nw = (int64_t)gridDim.x * 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + wid;
+  const int64_t u0 = gw * total / nw, u1 = (gw + 1) * total / nw;
+  if (u0 >= u1) return;  // no barrier follows
 
-  int cur_b = -1;
-  f16x8 qop[4];
-  float qs0 = 0.f, qs1 = 0.f, qe0 = 0.f, qe1 = 0.f, unscale = 1.f;
-  int len_n = 0, r0 = 0, ql = 0, min_len = 0;
-
-  for (int64_t u = u_begin + wid; u < u_end; u += 4) {
-    while (b + 1 < a.num_reqs && u >= a.req_blk[b + 1]) ++b;
-    const int j = (int)(u - a.req_blk[b]);
-    if (j >= a.max_blocks) {  // the request is longer than the table: never read past it
-      if (lane == 0) set_status(a.status, kDevBadLength);
-      continue;
+  auto req_of = [&](int64_t u) {  // largest b with s_blk[b] <= u
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_blk[mid] <= u) lo = mid; else hi = mid - 1;
     }
+    return lo;
+  };
 
-    if (b != cur_b) {  // query tile of request b (rows r0 .. r0 + ql - 1)
-      cur_b = b;
-      r0 = a.cu_q[b];
-      ql = a.cu_q[b + 1] - r0;
-      min_len = a.row_len[r0];
-      len_n = n < ql ? a.row_len[r0 + n] : 0;
-      u32x4 raw[4] = {};
-      if (n < ql) {
-        const uint16_t* qp = a.q_idx + (int64_t)(r0 + n) * a.q_stride + 32 * G;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+  QueryTile qt;
+  qt.b = -1;
+  PageBuf pa, pb;
+  int b = req_of(u0);
+  for (int64_t c0 = u0; c0 < u1; c0 += 64) {
+    const int cnt = (int)min((int64_t)64, u1 - c0);
+    // lane i: page of unit c0 + i (-1 when unusable)
+    int my_page = -1;
+    if (lane < cnt) {
+      const int64_t u = c0 + lane;
+      const int bl = req_of(u);
+      const int jl = (int)(u - s_blk[bl]);
+      if (jl < a.max_blocks) {
+        const int pg = a.block_table[(int64_t)bl * a.bt_stride + jl];
+        my_page = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+        if (my_page < 0) set_status(a.status, kDevBadPage);
+      } else {
+        set_status(a.status, kDevBadLength);
       }
-      uint32_t mx = 0;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) mx = max(mx, max(raw[s][w] & 0x7FFFu, (raw[s][w] >> 16) & 0x7FFFu));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
-      mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
-      int P = mx ? 13 - bf16_floor_log2(mx) : 0;
-      P = P > 64 ? 64 : (P < -64 ? -64 : P);
-      unscale = __builtin_ldexpf(1.0f, -P);
-      qs0 = qs1 = qe0 = qe1 = 0.f;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
-          const float x = __builtin_ldexpf(bf16_bits_to_f32(bits), P);
-          const _Float16 h = (_Float16)x;
-          const float err = fabsf(x - (float)h);
-          qop[s][e] = h;
-          if (FMT == 1 && s >= 2) { qs1 += fabsf((float)h); qe1 += err; }
-          else { qs0 += fabsf((float)h); qe0 += err; }
+    }
+    int pg0 = __builtin_amdgcn_readlane(my_page, 0);
+    if (pg0 >= 0) load_page<FMT>(pa, a, pg0, n, G);
+    for (int i = 0; i < cnt; i += 2) {
+      // unit c0 + i is in pa; issue c0 + i + 1 into pb
+      const int pg1 = i + 1 < cnt ? __builtin_amdgcn_readlane(my_page, i + 1) : -1;
+      if (pg1 >= 0) load_page<FMT>(pb, a, pg1, n, G);
+      {
+        const int64_t u = c0 + i;
+        while (b + 1 < B && u >= s_blk[b + 1]) ++b;
+        const int j = (int)(u - s_blk[b]);
+        if (j < a.max_blocks) {
+          if (b != qt.b) load_query<FMT>(qt, a, b, n, G);
+          if (pg0 >= 0) {
+            score_page<FMT>(pa, qt, a, j, n, G);
+          } else if (G == 0 && n < qt.ql) {
+            const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + j;
+            a.ws_score[o] = -INFINITY;
+            a.ws_bound[o] = 0.f;
+          }
         }
       }
-    }
-
-    const int page = a.block_table[(int64_t)b * a.bt_stride + j];
-    float* dst_s = a.ws_score + (int64_t)(r0 + n) * a.max_blocks + j;
-    float* dst_b = a.ws_bound + (int64_t)(r0 + n) * a.max_blocks + j;
-    if (page < 0 || page >= a.num_pages) {
-      if (lane == 0) set_status(a.status, kDevBadPage);
-      if (G == 0 && n < ql) { *dst_s = -INFINITY; *dst_b = 0.f; }
-      continue;
-    }
-    const uint8_t* pay = a.idx_data + (int64_t)page * (kPage * kPayload);
-    const uint8_t* scb = a.idx_scale + (int64_t)page * (kPage * SB);
-    u32x4 kr[8];
-    uint32_t ksb[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = *reinterpret_cast<const u32x4*>(pay + (16 * i + n) * kPayload + 16 * G);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (FMT == 1) ksb[i] = *reinterpret_cast<const uint16_t*>(scb + (16 * i + n) * SB + 2 * G);
-      else ksb[i] = scb[(16 * i + n) * SB + G];
-    }
-
-    const bool need_mask = (j + 1) * kPage > min_len;
-    float run = -INFINITY;
-    uint32_t sm0 = 0, sm1 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      typename Dec::scale_t s0, s1;
-      if (FMT == 1) {
-        const uint32_t b0 = ksb[i] & 0xFFu, b1 = ksb[i] >> 8;
-        sm0 = max(sm0, b0);
-        sm1 = max(sm1, b1);
-        s0 = Dec::scale(b0);
-        s1 = Dec::scale(b1);
-      } else {
-        sm0 = max(sm0, ksb[i]);
-        s0 = s1 = Dec::scale(ksb[i]);
+      if (i + 1 >= cnt) break;
+      pg0 = i + 2 < cnt ? __builtin_amdgcn_readlane(my_page, i + 2) : -1;
+      if (pg0 >= 0) load_page<FMT>(pa, a, pg0, n, G);
+      {
+        const int64_t u = c0 + i + 1;
+        while (b + 1 < B && u >= s_blk[b + 1]) ++b;
+        const int j = (int)(u - s_blk[b]);
+        if (j < a.max_blocks) {
+          if (b != qt.b) load_query<FMT>(qt, a, b, n, G);
+          if (pg1 >= 0) {
+            score_page<FMT>(pb, qt, a, j, n, G);
+          } else if (G == 0 && n < qt.ql) {
+            const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + j;
+            a.ws_score[o] = -INFINITY;
+            a.ws_bound[o] = 0.f;
+          }
+        }
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma_f16(Dec::run(kr[i][s], s < 2 ? s0 : s1), qop[s], acc);
-      if (need_mask) {
-        const int t0 = j * kPage + 16 * i + 4 * G;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (t0 + v >= len_n) acc[v] = -INFINITY;
-      }
-      run = fmaxf(run, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-    }
-    run = fmaxf(run, __shfl_xor(run, 16, 64));
-    run = fmaxf(run, __shfl_xor(run, 32, 64));
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      sm0 = max(sm0, (uint32_t)__shfl_xor((int)sm0, m, 64));
-      sm1 = max(sm1, (uint32_t)__shfl_xor((int)sm1, m, 64));
-    }
-    float part;
-    if (FMT == 1)
-      part = 6.0f * (e4m3_to_f32(sm0) * (kAccRel * qs0 + qe0) + e4m3_to_f32(sm1) * (kAccRel * qs1 + qe1));
-    else
-      part = 6.0f * e8m0_to_f32(sm0) * (kAccRel * qs0 + qe0);
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if (G == 0 && n < ql) {
-      *dst_s = run * unscale;
-      *dst_b = part * unscale * (1.0f + 0x1p-10f);
     }
   }
 }
@@ -206,294 +278,456 @@ __device__ __forceinline__ uint64_t comp_key(uint32_t key, int j, int tie_high) 
   return ((uint64_t)key << 32) | (uint32_t)(tie_high ? (uint32_t)j : ~(uint32_t)j);
 }
 
-struct SelectShared {
-  uint32_t key[kMaxBlocks];
-  uint8_t flag[kMaxBlocks];
-  uint32_t hist[256];
-  int band[kBandCap];
-  double exact[kBandCap];
-  double q[kDim];
-  uint64_t red64[4];
-  double redd[4];
-  float redf[4];
-  int redi[8];
-  int misc[4];
-  int scan[4];
-};
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)x, m, 64);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(x >> 32), m, 64);
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)x, src, 64);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(x >> 32), src, 64);
   return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) { return lane_max<1, 64>(x); }
+__device__ __forceinline__ int wave_sum_i(int x) { return lane_sum<1, 64>(x); }
 
-// k-th largest (1-based) composite key among j < n (keys are distinct).
-__device__ uint64_t select_kth(SelectShared& sh, int n, int kth, int tie_high) {
-  const int tid = threadIdx.x;
-  uint64_t prefix = 0, mask = 0;
-  int kk = kth;
-  for (int d = 56; d >= 0; d -= 8) {
-    sh.hist[tid] = 0;
-    __syncthreads();
-    for (int j = tid; j < n; j += 256) {
-      const uint64_t c = comp_key(sh.key[j], j, tie_high);
-      if ((c & mask) == prefix) atomicAdd(&sh.hist[(c >> d) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid < 64) {
-      const int L = tid;
-      const int c0 = sh.hist[255 - 4 * L], c1 = sh.hist[254 - 4 * L];
-      const int c2 = sh.hist[253 - 4 * L], c3 = sh.hist[252 - 4 * L];
-      const int sum = c0 + c1 + c2 + c3;
-      int incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off, 64);
-        if (L >= off) incl += y;
-      }
-      const int above = incl - sum;
-      if (above < kk && kk <= incl) {
-        int acc = above, digit, cnt;
-        if (kk <= acc + c0) { digit = 255 - 4 * L; cnt = c0; }
-        else if (kk <= acc + c0 + c1) { acc += c0; digit = 254 - 4 * L; cnt = c1; }
-        else if (kk <= acc + c0 + c1 + c2) { acc += c0 + c1; digit = 253 - 4 * L; cnt = c2; }
-        else { acc += c0 + c1 + c2; digit = 252 - 4 * L; cnt = c3; }
-        sh.misc[0] = digit;
-        sh.misc[1] = kk - acc;
-        sh.misc[2] = cnt;
-      }
-    }
-    __syncthreads();
-    const int digit = sh.misc[0], cnt = sh.misc[2];
-    kk = sh.misc[1];
-    prefix |= (uint64_t)digit << d;
-    mask |= (uint64_t)0xFF << d;
-    __syncthreads();
-    if (cnt == 1) {
-      for (int j = tid; j < n; j += 256) {
-        const uint64_t c = comp_key(sh.key[j], j, tie_high);
-        if ((c & mask) == prefix) sh.red64[0] = c;
-      }
-      __syncthreads();
-      const uint64_t res = sh.red64[0];
-      __syncthreads();
-      return res;
-    }
+// Bitonic network over one u64 per lane, descending across the wave.
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint64_t bitonic_steps(uint64_t x) {
+  if constexpr (STRIDE == 0) {
+    return x;
+  } else {
+    const int lane = threadIdx.x & 63;
+    const uint64_t o = lane_xor<STRIDE>(x);
+    const bool lower = (lane & STRIDE) == 0;       // first element of the pair
+    const bool desc = (lane & SIZE) == 0;          // direction of this bitonic block (all at SIZE 64)
+    x = (lower == desc) ? (o > x ? o : x) : (o < x ? o : x);
+    return bitonic_steps<SIZE, STRIDE / 2>(x);
   }
-  return prefix;
 }
+template <int SIZE>
+__device__ __forceinline__ uint64_t bitonic_sizes(uint64_t x) {
+  if constexpr (SIZE > 64) {
+    return x;
+  } else {
+    return bitonic_sizes<SIZE * 2>(bitonic_steps<SIZE, SIZE / 2>(x));
+  }
+}
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) { return bitonic_sizes<2>(x); }
 
-// Exact float64 score of block j of a row (-inf for an unusable page).
+// Exact float64 score of block j of a row, computed by one wave (-inf for an
+// unusable page). Lane l owns tokens l and l + 64. Every term q_d * k_d is exact
+// (<= 8 + 6 significant bits); the float64 sum is exact when the sum of |terms|
+// stays below 2^53 times the smallest unit in the last place among the terms,
+// which each token checks (M3S_DEV_INEXACT otherwise).
 template <int FMT>
-__device__ double exact_block_score(const IndexArgs& a, SelectShared& sh, int b, int j, int len, int lq) {
+__device__ double wave_exact_block_score(const IndexArgs& a, const double* sq, int b, int j, int len, int lq) {
   constexpr int SB = FMT == 1 ? 8 : 4;
-  const int tid = threadIdx.x, t = tid >> 1, h = tid & 1;
+  const int lane = threadIdx.x & 63;
   const int page = a.block_table[(int64_t)b * a.bt_stride + j];
-  const bool page_ok = page >= 0 && page < a.num_pages;
-  const bool valid = page_ok && (j * kPage + t < len);
-  double acc = 0.0, mag = 0.0;
-  int lk = INT_MAX;
-  if (page_ok) {
-    const uint8_t* p = a.idx_data + (int64_t)page * (kPage * kPayload) + t * kPayload + 32 * h;
-    const u32x4 w0 = *reinterpret_cast<const u32x4*>(p);
-    const u32x4 w1 = *reinterpret_cast<const u32x4*>(p + 16);
-    const uint8_t* sp = a.idx_scale + (int64_t)page * (kPage * SB) + t * SB + (SB / 2) * h;
-    double sv[4];
-    const int ng = FMT == 1 ? 4 : 2;
-    for (int g = 0; g < ng; ++g) {
-      const uint32_t byte = sp[g];
-      double s;
+  if (page < 0 || page >= a.num_pages) return -INFINITY;
+  const uint8_t* pbase = a.idx_data + (int64_t)page * (kPage * kPayload);
+  const uint8_t* sbase = a.idx_scale + (int64_t)page * (kPage * SB);
+  double best = -INFINITY;
+  bool inexact = false;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    const int t = lane + 64 * h;
+    u32x4 w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = *reinterpret_cast<const u32x4*>(pbase + t * kPayload + 16 * c);
+    double sv[SB];
+    int lk = INT_MAX;
+#pragma unroll
+    for (int g = 0; g < SB; ++g) {
+      const uint32_t byte = sbase[t * SB + g];
       int lsb;
       if (FMT == 1) {
         const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
         const uint32_t M = e ? (m | 8u) : m;
         const int ex = e ? (int)e - 10 : -9;
-        s = __builtin_ldexp((double)M, ex);
+        sv[g] = __builtin_ldexp((double)M, ex);
         lsb = M ? ex + __builtin_ctz(M) : INT_MAX;
       } else {
-        s = __builtin_ldexp(1.0, (int)byte - 127);
+        sv[g] = __builtin_ldexp(1.0, (int)byte - 127);
         lsb = (int)byte - 127;
       }
-      sv[g] = s;
       if (lsb != INT_MAX) lk = min(lk, lsb - 1);  // codes are multiples of 1/2
     }
-    const double tab[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-    for (int dd = 0; dd < 64; ++dd) {
-      const uint32_t word = dd < 32 ? w0[dd >> 3] : w1[(dd - 32) >> 3];
-      const uint32_t code = (word >> (4 * (dd & 7))) & 15u;
-      const double kv = (code & 8u ? -tab[code & 7u] : tab[code & 7u]) * sv[FMT == 1 ? (dd >> 4) : (dd >> 5)];
-      const double qv = sh.q[64 * h + dd];
-      acc = __builtin_fma(qv, kv, acc);
-      mag += fabs(qv) * fabs(kv);
-    }
-  }
-  acc += __shfl_xor(acc, 1, 64);
-  mag += __shfl_xor(mag, 1, 64);
-  lk = min(lk, __shfl_xor(lk, 1, 64));
-  if (valid && mag > 0.0 && lk != INT_MAX) {
-    const double lim = __builtin_ldexp(1.0, 53 + lq + lk);
-    if (!(mag * (1.0 + 0x1p-40) < lim)) set_status(a.status, kDevInexact);
-  }
-  double v = valid ? acc + 0.0 : -INFINITY;
+    double acc = 0.0, mag = 0.0;
+#pragma unroll 1
+    for (int c = 0; c < 4; ++c)
+#pragma unroll 2
+      for (int wi = 0; wi < 4; ++wi) {
+        const uint32_t word = w[c][wi];
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = fmax(v, __shfl_xor(v, m, 64));
-  __syncthreads();
-  if ((tid & 63) == 0) sh.redd[tid >> 6] = v;
-  __syncthreads();
-  const double r = fmax(fmax(sh.redd[0], sh.redd[1]), fmax(sh.redd[2], sh.redd[3]));
-  __syncthreads();
-  return r;
+        for (int bs = 0; bs < 4; ++bs) {
+          float2 pr;
+          switch (bs) {
+            case 0: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); pr = make_float2(x[0], x[1]); break; }
+            case 1: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); pr = make_float2(x[0], x[1]); break; }
+            case 2: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); pr = make_float2(x[0], x[1]); break; }
+            default: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); pr = make_float2(x[0], x[1]); break; }
+          }
+          const int d = 32 * c + 8 * wi + 2 * bs;
+          const double s = sv[FMT == 1 ? (d >> 4) : (d >> 5)];
+          const double k0 = (double)pr.x * s, k1 = (double)pr.y * s;
+          acc = __builtin_fma(sq[d], k0, acc);
+          acc = __builtin_fma(sq[d + 1], k1, acc);
+          mag = __builtin_fma(fabs(sq[d]), fabs(k0), mag);
+          mag = __builtin_fma(fabs(sq[d + 1]), fabs(k1), mag);
+        }
+      }
+    const bool valid = j * kPage + t < len;
+    if (valid && mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
+      inexact = true;
+    if (valid) best = fmax(best, acc + 0.0);
+  }
+  if (inexact) set_status(a.status, kDevInexact);
+  return lane_reduce<1, 64>(best, [](double x, double y) { return fmax(x, y); });
+}
+
+// Select: one 256-thread workgroup per row, every phase spread over all
+// threads, all global loads issued up front.
+//   0. thread t holds the scores of blocks j = t + 256 i in registers; the row's
+//      q, its block-table row and its largest error bound are loaded alongside;
+//   1. keys (score, tie-rule id): each wave bitonic-sorts its 64 thread maxima;
+//      the largest of the four (k+1)-th values is a threshold that keeps the k+1
+//      best keys; the keys above it (usually < 64) are sorted by one wave, giving
+//      the k-th and (k+1)-th keys exactly (an iterative extraction covers larger
+//      sets and k = 64);
+//   2. certification against the row's error bound: blocks above hi are in,
+//      below lo out, the band between is rescored in exact float64 by all
+//      threads at once (one half-token of one band block per work item);
+//   3. the open slots are filled by (exact score, tie rule) and the ids emitted
+//      in ascending order from a bitmap.
+constexpr int kSelPer = kMaxBlocks / 256;  // score registers per thread
+
+struct SelectShared {
+  uint32_t bits[kMaxBlocks / 32];
+  int bt[kMaxBlocks];
+  uint64_t wave_theta[4];
+  uint64_t cand[64];
+  int band[kBandCap];
+  double dots[kBandCap];      // exact score of each band block (max over tokens)
+  double q[kDim];
+  float red[4];
+  int ired[4];
+  int counters[4];            // candidates, in, band
+  uint64_t keys[2];
+  int mode;
+};
+
+// float64 max via integer atomics on LDS: valid for finite doubles and -inf
+__device__ __forceinline__ void lds_max_f64(double* p, double v) {
+  unsigned long long* u = reinterpret_cast<unsigned long long*>(p);
+  unsigned long long cur = *u;
+  while (true) {
+    const double c = __longlong_as_double((long long)cur);
+    if (!(v > c)) break;
+    const unsigned long long prev = atomicCAS(u, cur, (unsigned long long)__double_as_longlong(v));
+    if (prev == cur) break;
+    cur = prev;
+  }
 }
 
 template <int FMT>
 __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
+  constexpr int SB = FMT == 1 ? 8 : 4;
   __shared__ SelectShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = blockIdx.x;
   const int k = a.topk;
+  const int th = a.tie_high;
   int32_t* out = a.topk_ids + (int64_t)r * k;
   const int b = a.row_req[r];
   const int len = a.row_len[r];
-  if (b < 0) {
-    for (int i = tid; i < k; i += 256) out[i] = -1;
-    return;
-  }
   const int nb = (len + kPage - 1) / kPage;
-  if (len <= 0 || nb > a.max_blocks) {
-    if (tid == 0) set_status(a.status, kDevBadLength);
-    for (int i = tid; i < k; i += 256) out[i] = -1;
+  if (b < 0 || len <= 0 || nb > a.max_blocks || nb <= k) {
+    if (b >= 0 && (len <= 0 || nb > a.max_blocks) && tid == 0) set_status(a.status, kDevBadLength);
+    const bool all = b >= 0 && len > 0 && nb <= a.max_blocks;
+    if (tid < k) out[tid] = (all && tid < nb) ? tid : -1;
     return;
   }
-  if (nb <= k) {
-    for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
-    return;
-  }
-  const int th = a.tie_high;
+  // 0. loads
   const float* sc = a.ws_score + (int64_t)r * a.max_blocks;
   const float* bd = a.ws_bound + (int64_t)r * a.max_blocks;
-  float dmax = 0.f;
-  for (int j = tid; j < nb; j += 256) {
-    sh.key[j] = ord_f32(sc[j]);
-    sh.flag[j] = 0;
-    dmax = fmaxf(dmax, bd[j]);
-  }
+  float sv[kSelPer];
+  float dm = 0.f;
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) dmax = fmaxf(dmax, __shfl_xor(dmax, m, 64));
-  if (lane == 0) sh.redf[wid] = dmax;
-  if (tid == 0) { sh.misc[3] = 0; sh.redi[0] = 0; sh.redi[1] = 0; }
-  __syncthreads();
-  dmax = fmaxf(fmaxf(sh.redf[0], sh.redf[1]), fmaxf(sh.redf[2], sh.redf[3]));
-
-  // (k+1)-th and k-th largest composite keys
-  const uint64_t K1 = select_kth(sh, nb, k + 1, th);
-  uint64_t mn = ~(uint64_t)0;
-  for (int j = tid; j < nb; j += 256) {
-    const uint64_t c = comp_key(sh.key[j], j, th);
-    if (c > K1 && c < mn) mn = c;
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const uint64_t o = shfl_xor_u64(mn, m);
-    mn = o < mn ? o : mn;
-  }
-  if (lane == 0) sh.red64[wid] = mn;
-  __syncthreads();
-  uint64_t Kk = sh.red64[0];
-  for (int w = 1; w < 4; ++w) Kk = sh.red64[w] < Kk ? sh.red64[w] : Kk;
-  __syncthreads();
-
-  bool by_key = dmax == 0.f;  // exact scores: select by composite key directly
-  if (!by_key) {
-    const double T = (double)unord_f32((uint32_t)(Kk >> 32));
-    const double S1 = (double)unord_f32((uint32_t)(K1 >> 32));
-    const double lo = T - 2.0 * (double)dmax, hi = S1 + 2.0 * (double)dmax;
-    for (int j = tid; j < nb; j += 256) {
-      const double s = (double)unord_f32(sh.key[j]);
-      if (s > hi) {
-        sh.flag[j] = 1;
-        atomicAdd(&sh.redi[0], 1);
-      } else if (s >= lo) {
-        const int slot = atomicAdd(&sh.redi[1], 1);
-        if (slot < kBandCap) sh.band[slot] = j;
-      }
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = tid + 256 * i;
+    sv[i] = -INFINITY;
+    if (j < nb) {
+      sv[i] = sc[j] + 0.0f;
+      dm = fmaxf(dm, bd[j]);
     }
-    __syncthreads();
-    const int nin = sh.redi[0], nband = sh.redi[1];
-    const int need = k - nin;
-    if (nband == need) {
-      for (int i = tid; i < nband; i += 256) sh.flag[sh.band[i]] = 1;
-    } else if (nband > kBandCap || need < 0) {
-      if (tid == 0) set_status(a.status, kDevBandOverflow);
-      for (int j = tid; j < nb; j += 256) sh.flag[j] = 0;
-      by_key = true;
-    } else {
-      // exact rescore of the band
-      const uint16_t* qp = a.q_idx + (int64_t)r * a.q_stride;
-      int lqv = INT_MAX;
-      if (tid < kDim) {
-        const uint32_t bits = qp[tid];
-        sh.q[tid] = (double)bf16_bits_to_f32(bits);
-        const uint32_t m = bits & 0x7FFFu;
-        if (m) {
-          const uint32_t ex = m >> 7, mant = m & 0x7Fu;
-          const uint32_t M = ex ? (mant | 0x80u) : mant;
-          const int e = ex ? (int)ex - 134 : -133;
-          lqv = e + __builtin_ctz(M);
+  }
+  for (int j = tid; j < nb; j += 256) sh.bt[j] = a.block_table[(int64_t)b * a.bt_stride + j];
+  int lqv = INT_MAX;
+  if (tid < kDim) {
+    const uint32_t bits = a.q_idx[(int64_t)r * a.q_stride + tid];
+    sh.q[tid] = (double)bf16_bits_to_f32(bits);
+    const uint32_t m = bits & 0x7FFFu;
+    if (m) {
+      const uint32_t ex = m >> 7, mant = m & 0x7Fu;
+      const uint32_t M = ex ? (mant | 0x80u) : mant;
+      lqv = (ex ? (int)ex - 134 : -133) + __builtin_ctz(M);
+    }
+  }
+  for (int i = tid; i < (nb + 31) / 32; i += 256) sh.bits[i] = 0u;
+  if (tid < 4) sh.counters[tid] = 0;
+  auto key_of = [&](int i) { return comp_key(ord_f32(sv[i]), tid + 256 * i, th); };
+
+  // 1a. per-wave thresholds from the thread maxima
+  uint64_t tmax = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i)
+    if (tid + 256 * i < nb) {
+      const uint64_t c = key_of(i);
+      tmax = c > tmax ? c : tmax;
+    }
+  dm = lane_fmax<1, 64>(dm);
+  lqv = lane_reduce<1, 64>(lqv, [](int x, int y) { return x < y ? x : y; });
+  // each wave's 16 largest thread maxima; the (k+1)-th largest of their union U
+  // is a valid threshold (U holds k+1 keys at or above it)
+  const bool small_k = k < 64;
+  {
+    const uint64_t srt = wave_sort_desc(tmax);
+    if (lane < 16) sh.cand[16 * w + lane] = srt;
+  }
+  if (lane == 0) {
+    sh.red[w] = dm;
+    sh.ired[w] = lqv;
+  }
+  __syncthreads();
+  const float dmax = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
+  int lq = min(min(sh.ired[0], sh.ired[1]), min(sh.ired[2], sh.ired[3]));
+  lq = lq == INT_MAX ? 0 : lq;
+  if (w == 0 && small_k) {
+    const uint64_t srt = wave_sort_desc(sh.cand[lane]);
+    const uint64_t th_k = shfl_u64(srt, k);
+    if (lane == 0) sh.wave_theta[0] = th_k;
+  }
+  __syncthreads();
+  uint64_t theta = 0;
+  if (small_k) {
+    theta = sh.wave_theta[0];
+    // 1b. compact the keys >= theta
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i)
+      if (tid + 256 * i < nb) {
+        const uint64_t c = key_of(i);
+        if (c >= theta) {
+          const int slot = atomicAdd(&sh.counters[0], 1);
+          if (slot < 64) sh.cand[slot] = c;
         }
       }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) lqv = min(lqv, __shfl_xor(lqv, m, 64));
-      if (lane == 0) sh.redi[2 + wid] = lqv;
-      __syncthreads();
-      const int lq = min(min(sh.redi[2], sh.redi[3]), min(sh.redi[4], sh.redi[5]));
-      for (int i = 0; i < nband; ++i) {
-        const double e = exact_block_score<FMT>(a, sh, b, sh.band[i], len, lq == INT_MAX ? 0 : lq);
-        if (tid == 0) sh.exact[i] = e + 0.0;
+  }
+  __syncthreads();
+  const int ncand = sh.counters[0];
+  if (small_k && ncand <= 64) {
+    if (w == 0) {
+      const uint64_t srt = wave_sort_desc(lane < ncand ? sh.cand[lane] : 0);
+      const uint64_t Kk = shfl_u64(srt, k - 1), K1 = shfl_u64(srt, k);
+      if (lane == 0) {
+        sh.keys[0] = Kk;
+        sh.keys[1] = K1;
       }
+    }
+  } else {  // iterative extraction of the k+1 best keys over the register-held keys
+    uint64_t prev = ~(uint64_t)0;
+    for (int t = 0; t <= k; ++t) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < kSelPer; ++i)
+        if (tid + 256 * i < nb) {
+          const uint64_t c = key_of(i);
+          if (c < prev && c > best) best = c;
+        }
+      best = wave_max_u64(best);
+      if (lane == 0) sh.wave_theta[w] = best;
       __syncthreads();
+      best = sh.wave_theta[0];
+      for (int q4 = 1; q4 < 4; ++q4) best = sh.wave_theta[q4] > best ? sh.wave_theta[q4] : best;
+      if (tid == 0) {
+        if (t == k - 1) sh.keys[0] = best;
+        sh.keys[1] = best;
+      }
+      prev = best;
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  const uint64_t Kk = sh.keys[0], K1 = sh.keys[1];
+
+  // 2. certification
+  int mode = 0;  // 0: select by key (exact scores); 1: score >= lo; 2: > hi or rescored
+  double lo = 0.0, hi = 0.0;
+  if (dmax > 0.f) {
+    lo = (double)unord_f32((uint32_t)(Kk >> 32)) - 2.0 * (double)dmax;
+    hi = (double)unord_f32((uint32_t)(K1 >> 32)) + 2.0 * (double)dmax;
+    int nin = 0;
+#pragma unroll
+    for (int i = 0; i < kSelPer; ++i)
+      if (tid + 256 * i < nb) {
+        const double s_ = (double)sv[i];
+        if (s_ > hi) {
+          ++nin;
+        } else if (s_ >= lo) {
+          const int slot = atomicAdd(&sh.counters[2], 1);
+          if (slot < kBandCap) {
+            sh.band[slot] = tid + 256 * i;
+            sh.dots[slot] = -INFINITY;
+          }
+        }
+      }
+    nin = lane_sum<1, 64>(nin);
+    if (lane == 0) atomicAdd(&sh.counters[1], nin);
+    __syncthreads();
+    const int nband = sh.counters[2], need = k - sh.counters[1];
+    if (nband == need) {
+      mode = 1;
+    } else if (nband > kBandCap) {
+      if (tid == 0) set_status(a.status, kDevBandOverflow);
+      mode = 0;
+    } else {
+      mode = 2;
+      // exact rescore: work item = (band block, token, half of the dims); each
+      // thread loads up to four items before computing any of them
+      bool inexact = false;
+      constexpr int kBatch = 4;
+      for (int m0 = 0; m0 < nband; m0 += kBatch) {
+        u32x4 w0[kBatch], w1[kBatch];
+        uint32_t sb4[kBatch];
+        int pg[kBatch];
+        const int t = tid >> 1, h = tid & 1;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int m = m0 + u;
+          pg[u] = -1;
+          if (m < nband) {
+            const int page = sh.bt[sh.band[m]];
+            if (page >= 0 && page < a.num_pages) {
+              pg[u] = page;
+              const uint8_t* pp = a.idx_data + (int64_t)page * (kPage * kPayload) + t * kPayload + 32 * h;
+              w0[u] = *reinterpret_cast<const u32x4*>(pp);
+              w1[u] = *reinterpret_cast<const u32x4*>(pp + 16);
+              const uint8_t* spp = a.idx_scale + (int64_t)page * (kPage * SB) + t * SB + (SB / 2) * h;
+              sb4[u] = FMT == 1 ? *reinterpret_cast<const uint32_t*>(spp) : (uint32_t)*reinterpret_cast<const uint16_t*>(spp);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int m = m0 + u;
+          if (m >= nband) break;  // uniform
+          const int j = sh.band[m];
+          double acc = 0.0, mag = 0.0;
+          int lk = INT_MAX;
+          if (pg[u] >= 0) {
+            double svd[SB / 2];
+#pragma unroll
+            for (int g = 0; g < SB / 2; ++g) {
+              const uint32_t byte = (sb4[u] >> (8 * g)) & 0xFFu;
+              int lsb;
+              if (FMT == 1) {
+                const uint32_t e = (byte >> 3) & 15u, mm = byte & 7u;
+                const uint32_t M = e ? (mm | 8u) : mm;
+                const int ex = e ? (int)e - 10 : -9;
+                svd[g] = __builtin_ldexp((double)M, ex);
+                lsb = M ? ex + __builtin_ctz(M) : INT_MAX;
+              } else {
+                svd[g] = __builtin_ldexp(1.0, (int)byte - 127);
+                lsb = (int)byte - 127;
+              }
+              if (lsb != INT_MAX) lk = min(lk, lsb - 1);
+            }
+#pragma unroll
+            for (int wi = 0; wi < 8; ++wi) {
+              const uint32_t word = wi < 4 ? w0[u][wi] : w1[u][wi - 4];
+#pragma unroll
+              for (int bs = 0; bs < 4; ++bs) {
+                float2 pr;
+                switch (bs) {
+                  case 0: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); pr = make_float2(x[0], x[1]); break; }
+                  case 1: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); pr = make_float2(x[0], x[1]); break; }
+                  case 2: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); pr = make_float2(x[0], x[1]); break; }
+                  default: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); pr = make_float2(x[0], x[1]); break; }
+                }
+                const int dd = 8 * wi + 2 * bs;  // dim within the half
+                const double s_ = svd[FMT == 1 ? (dd >> 4) : (dd >> 5)];
+                const double k0 = (double)pr.x * s_, k1 = (double)pr.y * s_;
+                const double q0 = sh.q[64 * h + dd], q1 = sh.q[64 * h + dd + 1];
+                acc = __builtin_fma(q0, k0, acc);
+                acc = __builtin_fma(q1, k1, acc);
+                mag = __builtin_fma(fabs(q0), fabs(k0), mag);
+                mag = __builtin_fma(fabs(q1), fabs(k1), mag);
+              }
+            }
+          }
+          // the two halves of a token sit in lanes 2u, 2u + 1
+          acc += lane_xor<1>(acc);
+          mag += lane_xor<1>(mag);
+          lk = min(lk, lane_xor<1>(lk));
+          const bool valid = pg[u] >= 0 && (j * kPage + t < len);
+          if (valid && mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
+            inexact = true;
+          double v = valid ? acc + 0.0 : -INFINITY;
+          v = lane_reduce<1, 64>(v, [](double x, double y) { return fmax(x, y); });  // 32 tokens of block m
+          if (lane == 0) lds_max_f64(&sh.dots[m], v);
+        }
+      }
+      if (inexact) set_status(a.status, kDevInexact);
+      __syncthreads();
+      // fill the open slots by (exact score, tie-rule id)
       for (int i = tid; i < nband; i += 256) {
-        const double ei = sh.exact[i];
+        const double ei = sh.dots[i] + 0.0;
         const int ji = sh.band[i];
         const uint32_t ki = th ? (uint32_t)ji : ~(uint32_t)ji;
         int rank = 0;
         for (int m = 0; m < nband; ++m) {
-          const double em = sh.exact[m];
-          const uint32_t km = th ? (uint32_t)sh.band[m] : ~(uint32_t)sh.band[m];
+          const double em = sh.dots[m] + 0.0;
+          const int jm = sh.band[m];
+          const uint32_t km = th ? (uint32_t)jm : ~(uint32_t)jm;
           rank += (em > ei) || (em == ei && km > ki);
         }
-        if (rank < need) sh.flag[ji] = 1;
+        if (rank < need) atomicOr(&sh.bits[ji >> 5], 1u << (ji & 31));
       }
     }
   }
-  __syncthreads();
-  if (by_key) {
-    for (int j = tid; j < nb; j += 256) sh.flag[j] = comp_key(sh.key[j], j, th) >= Kk ? 1 : 0;
-    __syncthreads();
-  }
-
-  // ascending compaction of the selected ids
-  const int per = (nb + 255) / 256;
-  const int j0 = min(nb, tid * per), j1 = min(nb, j0 + per);
-  int cnt = 0;
-  for (int j = j0; j < j1; ++j) cnt += sh.flag[j];
-  int incl = cnt;
+  // 3. selection bitmap, then ascending emission by wave 0
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) sh.scan[wid] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wid; ++w) base += sh.scan[w];
-  const int total = sh.scan[0] + sh.scan[1] + sh.scan[2] + sh.scan[3];
-  int pos = base + incl - cnt;
-  for (int j = j0; j < j1; ++j)
-    if (sh.flag[j]) {
-      if (pos < k) out[pos] = j;
-      ++pos;
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = tid + 256 * i;
+    if (j < nb) {
+      bool sel;
+      if (mode == 0) sel = key_of(i) >= Kk;
+      else if (mode == 1) sel = (double)sv[i] >= lo;
+      else sel = (double)sv[i] > hi;
+      if (sel) atomicOr(&sh.bits[j >> 5], 1u << (j & 31));
     }
-  for (int i = total + tid; i < k; i += 256) out[i] = -1;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  int pos = 0;
+  const int nwords = (nb + 31) / 32;
+  for (int w0 = 0; w0 < nwords; w0 += 64) {
+    const int wi = w0 + lane;
+    const uint32_t word = wi < nwords ? sh.bits[wi] : 0u;
+    const int c = __popc(word);
+    int incl = c;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    int p = pos + incl - c;
+    uint32_t m = word;
+    while (m) {
+      const int bit = __builtin_ctz(m);
+      m &= m - 1;
+      if (p < k) out[p] = 32 * wi + bit;
+      ++p;
+    }
+    pos += __shfl(incl, 63, 64);
+  }
+  for (int t = pos + lane; t < k; t += 64) out[t] = -1;
 }
 
 size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks) {

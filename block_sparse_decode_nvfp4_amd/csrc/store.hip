@@ -101,8 +101,8 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
   uint32_t amax = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) amax = max(amax, bits[e] & 0x7FFFu);
-  amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1, 64));
-  if (FMT == 2) amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2, 64));
+  amax = max(amax, lane_xor<1>(amax));
+  if (FMT == 2) amax = max(amax, lane_xor<2>(amax));
 
   uint32_t scale_byte;
   uint32_t packed = 0;
