@@ -284,7 +284,6 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
   return ((uint64_t)hi << 32) | lo;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) { return lane_max<1, 64>(x); }
-__device__ __forceinline__ int wave_sum_i(int x) { return lane_sum<1, 64>(x); }
 
 // Bitonic network over one u64 per lane, descending across the wave.
 template <int SIZE, int STRIDE>
@@ -310,110 +309,35 @@ __device__ __forceinline__ uint64_t bitonic_sizes(uint64_t x) {
 }
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) { return bitonic_sizes<2>(x); }
 
-// Exact float64 score of block j of a row, computed by one wave (-inf for an
-// unusable page). Lane l owns tokens l and l + 64. Every term q_d * k_d is exact
-// (<= 8 + 6 significant bits); the float64 sum is exact when the sum of |terms|
-// stays below 2^53 times the smallest unit in the last place among the terms,
-// which each token checks (M3S_DEV_INEXACT otherwise).
-template <int FMT>
-__device__ double wave_exact_block_score(const IndexArgs& a, const double* sq, int b, int j, int len, int lq) {
-  constexpr int SB = FMT == 1 ? 8 : 4;
-  const int lane = threadIdx.x & 63;
-  const int page = a.block_table[(int64_t)b * a.bt_stride + j];
-  if (page < 0 || page >= a.num_pages) return -INFINITY;
-  const uint8_t* pbase = a.idx_data + (int64_t)page * (kPage * kPayload);
-  const uint8_t* sbase = a.idx_scale + (int64_t)page * (kPage * SB);
-  double best = -INFINITY;
-  bool inexact = false;
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    const int t = lane + 64 * h;
-    u32x4 w[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) w[c] = *reinterpret_cast<const u32x4*>(pbase + t * kPayload + 16 * c);
-    double sv[SB];
-    int lk = INT_MAX;
-#pragma unroll
-    for (int g = 0; g < SB; ++g) {
-      const uint32_t byte = sbase[t * SB + g];
-      int lsb;
-      if (FMT == 1) {
-        const uint32_t e = (byte >> 3) & 15u, m = byte & 7u;
-        const uint32_t M = e ? (m | 8u) : m;
-        const int ex = e ? (int)e - 10 : -9;
-        sv[g] = __builtin_ldexp((double)M, ex);
-        lsb = M ? ex + __builtin_ctz(M) : INT_MAX;
-      } else {
-        sv[g] = __builtin_ldexp(1.0, (int)byte - 127);
-        lsb = (int)byte - 127;
-      }
-      if (lsb != INT_MAX) lk = min(lk, lsb - 1);  // codes are multiples of 1/2
-    }
-    double acc = 0.0, mag = 0.0;
-#pragma unroll 1
-    for (int c = 0; c < 4; ++c)
-#pragma unroll 2
-      for (int wi = 0; wi < 4; ++wi) {
-        const uint32_t word = w[c][wi];
-#pragma unroll
-        for (int bs = 0; bs < 4; ++bs) {
-          float2 pr;
-          switch (bs) {
-            case 0: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); pr = make_float2(x[0], x[1]); break; }
-            case 1: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); pr = make_float2(x[0], x[1]); break; }
-            case 2: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); pr = make_float2(x[0], x[1]); break; }
-            default: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); pr = make_float2(x[0], x[1]); break; }
-          }
-          const int d = 32 * c + 8 * wi + 2 * bs;
-          const double s = sv[FMT == 1 ? (d >> 4) : (d >> 5)];
-          const double k0 = (double)pr.x * s, k1 = (double)pr.y * s;
-          acc = __builtin_fma(sq[d], k0, acc);
-          acc = __builtin_fma(sq[d + 1], k1, acc);
-          mag = __builtin_fma(fabs(sq[d]), fabs(k0), mag);
-          mag = __builtin_fma(fabs(sq[d + 1]), fabs(k1), mag);
-        }
-      }
-    const bool valid = j * kPage + t < len;
-    if (valid && mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
-      inexact = true;
-    if (valid) best = fmax(best, acc + 0.0);
-  }
-  if (inexact) set_status(a.status, kDevInexact);
-  return lane_reduce<1, 64>(best, [](double x, double y) { return fmax(x, y); });
-}
-
-// Select: one 256-thread workgroup per row, every phase spread over all
-// threads, all global loads issued up front.
-//   0. thread t holds the scores of blocks j = t + 256 i in registers; the row's
-//      q, its block-table row and its largest error bound are loaded alongside;
-//   1. keys (score, tie-rule id): each wave bitonic-sorts its 64 thread maxima;
-//      the largest of the four (k+1)-th values is a threshold that keeps the k+1
-//      best keys; the keys above it (usually < 64) are sorted by one wave, giving
-//      the k-th and (k+1)-th keys exactly (an iterative extraction covers larger
-//      sets and k = 64);
+// Select: one 256-thread workgroup per row.
+//   0. the row's scores (thread t holds blocks j = t + 256 i), its largest
+//      error bound and its query are loaded at once (the row length only masks);
+//   1. threshold: each wave bitonic-sorts its 64 thread maxima (ordered score
+//      bits); with c = ceil((k+1)/4), every wave holds c keys at or above its
+//      c-th largest maximum, so the smallest of the four is at or below the
+//      (k+1)-th best key overall; the keys at or above it (usually < 64) are
+//      sorted by one wave, giving the k-th and (k+1)-th keys (score, tie-rule
+//      id) exactly; an iterative extraction covers larger sets and k = 64;
 //   2. certification against the row's error bound: blocks above hi are in,
-//      below lo out, the band between is rescored in exact float64 by all
-//      threads at once (one half-token of one band block per work item);
-//   3. the open slots are filled by (exact score, tie rule) and the ids emitted
-//      in ascending order from a bitmap.
+//      below lo out, and the band between is rescored in exact float64 by all
+//      threads at once when it does not exactly fill the open slots;
+//   3. a selection bitmap (one ballot word per 64 blocks), emitted ascending.
 constexpr int kSelPer = kMaxBlocks / 256;  // score registers per thread
 
 struct SelectShared {
-  uint32_t bits[kMaxBlocks / 32];
-  int bt[kMaxBlocks];
-  uint64_t wave_theta[4];
+  uint64_t sel[kMaxBlocks / 64];
   uint64_t cand[64];
   int band[kBandCap];
-  double dots[kBandCap];      // exact score of each band block (max over tokens)
+  double dots[kBandCap];
   double q[kDim];
+  uint32_t thr[4];
   float red[4];
   int ired[4];
-  int counters[4];            // candidates, in, band
+  int cnt[4];          // candidates, in, band
+  int wsum[8];
   uint64_t keys[2];
-  int mode;
 };
 
-// float64 max via integer atomics on LDS: valid for finite doubles and -inf
 __device__ __forceinline__ void lds_max_f64(double* p, double v) {
   unsigned long long* u = reinterpret_cast<unsigned long long*>(p);
   unsigned long long cur = *u;
@@ -426,6 +350,25 @@ __device__ __forceinline__ void lds_max_f64(double* p, double v) {
   }
 }
 
+// bitonic network over one u32 per lane, descending across the wave
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ uint32_t bitonic32_steps(uint32_t x) {
+  if constexpr (STRIDE == 0) {
+    return x;
+  } else {
+    const int lane = threadIdx.x & 63;
+    const uint32_t o = lane_xor<STRIDE>(x);
+    const bool keep_max = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);
+    x = keep_max ? max(o, x) : min(o, x);
+    return bitonic32_steps<SIZE, STRIDE / 2>(x);
+  }
+}
+template <int SIZE>
+__device__ __forceinline__ uint32_t bitonic32_sizes(uint32_t x) {
+  if constexpr (SIZE > 64) return x;
+  else return bitonic32_sizes<SIZE * 2>(bitonic32_steps<SIZE, SIZE / 2>(x));
+}
+
 template <int FMT>
 __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   constexpr int SB = FMT == 1 ? 8 : 4;
@@ -434,93 +377,112 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   const int r = blockIdx.x;
   const int k = a.topk;
   const int th = a.tie_high;
+  const int MB = a.max_blocks;
   int32_t* out = a.topk_ids + (int64_t)r * k;
+
+  // 0. loads, all issued together
+  const float* sc = a.ws_score + (int64_t)r * MB;
+  const float* bd = a.ws_bound + (int64_t)r * MB;
   const int b = a.row_req[r];
   const int len = a.row_len[r];
+  float sv[kSelPer], bv[kSelPer];
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = tid + 256 * i;
+    if (j >= MB) break;
+    sv[i] = sc[j];
+    bv[i] = bd[j];
+  }
+  uint32_t qbits = 0;
+  if (tid < kDim) qbits = a.q_idx[(int64_t)r * a.q_stride + tid];
   const int nb = (len + kPage - 1) / kPage;
-  if (b < 0 || len <= 0 || nb > a.max_blocks || nb <= k) {
-    if (b >= 0 && (len <= 0 || nb > a.max_blocks) && tid == 0) set_status(a.status, kDevBadLength);
-    const bool all = b >= 0 && len > 0 && nb <= a.max_blocks;
+  if (b < 0 || len <= 0 || nb > MB || nb <= k) {
+    if (b >= 0 && (len <= 0 || nb > MB) && tid == 0) set_status(a.status, kDevBadLength);
+    const bool all = b >= 0 && len > 0 && nb <= MB;
     if (tid < k) out[tid] = (all && tid < nb) ? tid : -1;
     return;
   }
-  // 0. loads
-  const float* sc = a.ws_score + (int64_t)r * a.max_blocks;
-  const float* bd = a.ws_bound + (int64_t)r * a.max_blocks;
-  float sv[kSelPer];
+  // blocks past the row's causal range were never scored: they never compete
+  // and their workspace entries are not read
   float dm = 0.f;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const int j = tid + 256 * i;
-    sv[i] = -INFINITY;
-    if (j < nb) {
-      sv[i] = sc[j] + 0.0f;
-      dm = fmaxf(dm, bd[j]);
-    }
+    if (j >= MB) break;
+    if (j >= nb) sv[i] = -INFINITY;
+    else dm = fmaxf(dm, bv[i]);
   }
-  for (int j = tid; j < nb; j += 256) sh.bt[j] = a.block_table[(int64_t)b * a.bt_stride + j];
+  auto okey = [&](int i) { return ord_f32(sv[i]); };
+  auto ckey = [&](int i) { return comp_key(ord_f32(sv[i]), tid + 256 * i, th); };
+
+  // 1. threshold from the per-wave sorted thread maxima
+  uint32_t tmax = 0;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = tid + 256 * i;
+    if (j >= nb) break;
+    tmax = max(tmax, okey(i));
+  }
   int lqv = INT_MAX;
   if (tid < kDim) {
-    const uint32_t bits = a.q_idx[(int64_t)r * a.q_stride + tid];
-    sh.q[tid] = (double)bf16_bits_to_f32(bits);
-    const uint32_t m = bits & 0x7FFFu;
+    sh.q[tid] = (double)bf16_bits_to_f32(qbits);
+    const uint32_t m = qbits & 0x7FFFu;
     if (m) {
       const uint32_t ex = m >> 7, mant = m & 0x7Fu;
       const uint32_t M = ex ? (mant | 0x80u) : mant;
       lqv = (ex ? (int)ex - 134 : -133) + __builtin_ctz(M);
     }
   }
-  for (int i = tid; i < (nb + 31) / 32; i += 256) sh.bits[i] = 0u;
-  if (tid < 4) sh.counters[tid] = 0;
-  auto key_of = [&](int i) { return comp_key(ord_f32(sv[i]), tid + 256 * i, th); };
-
-  // 1a. per-wave thresholds from the thread maxima
-  uint64_t tmax = 0;
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i)
-    if (tid + 256 * i < nb) {
-      const uint64_t c = key_of(i);
-      tmax = c > tmax ? c : tmax;
-    }
   dm = lane_fmax<1, 64>(dm);
   lqv = lane_reduce<1, 64>(lqv, [](int x, int y) { return x < y ? x : y; });
-  // each wave's 16 largest thread maxima; the (k+1)-th largest of their union U
-  // is a valid threshold (U holds k+1 keys at or above it)
+  // c_w keys taken from wave w: ceil((k+1)/4) each, moved to the earlier waves
+  // where a short row leaves a later wave fewer than that many live threads
   const bool small_k = k < 64;
+  int cw = 0;
   {
-    const uint64_t srt = wave_sort_desc(tmax);
-    if (lane < 16) sh.cand[16 * w + lane] = srt;
+    const int c = (k + 4) / 4;
+    int tot = 0;
+    for (int q4 = 0; q4 < 4; ++q4) tot += min(min(max(nb - 64 * q4, 0), 64), c);
+    int def = k + 1 - tot;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int n = min(max(nb - 64 * q4, 0), 64);
+      int cq = min(n, c);
+      const int add = min(def, n - cq);
+      cq += add;
+      def -= add;
+      if (q4 == w) cw = cq;
+    }
+  }
+  uint32_t theta_w = 0xFFFFFFFFu;
+  if (small_k) {
+    const uint32_t srt = bitonic32_sizes<2>(tmax);
+    if (cw > 0) theta_w = __shfl(srt, cw - 1, 64);
   }
   if (lane == 0) {
     sh.red[w] = dm;
     sh.ired[w] = lqv;
+    sh.thr[w] = theta_w;
   }
+  if (tid < 4) sh.cnt[tid] = 0;
+  for (int i = tid; i < (nb + 63) / 64; i += 256) sh.sel[i] = 0ull;
   __syncthreads();
   const float dmax = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
   int lq = min(min(sh.ired[0], sh.ired[1]), min(sh.ired[2], sh.ired[3]));
   lq = lq == INT_MAX ? 0 : lq;
-  if (w == 0 && small_k) {
-    const uint64_t srt = wave_sort_desc(sh.cand[lane]);
-    const uint64_t th_k = shfl_u64(srt, k);
-    if (lane == 0) sh.wave_theta[0] = th_k;
-  }
-  __syncthreads();
-  uint64_t theta = 0;
   if (small_k) {
-    theta = sh.wave_theta[0];
-    // 1b. compact the keys >= theta
+    const uint32_t theta = min(min(sh.thr[0], sh.thr[1]), min(sh.thr[2], sh.thr[3]));
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i)
-      if (tid + 256 * i < nb) {
-        const uint64_t c = key_of(i);
-        if (c >= theta) {
-          const int slot = atomicAdd(&sh.counters[0], 1);
-          if (slot < 64) sh.cand[slot] = c;
-        }
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = tid + 256 * i;
+      if (j >= nb) break;
+      if (okey(i) >= theta) {
+        const int slot = atomicAdd(&sh.cnt[0], 1);
+        if (slot < 64) sh.cand[slot] = ckey(i);
       }
+    }
   }
   __syncthreads();
-  const int ncand = sh.counters[0];
+  const int ncand = sh.cnt[0];
   if (small_k && ncand <= 64) {
     if (w == 0) {
       const uint64_t srt = wave_sort_desc(lane < ncand ? sh.cand[lane] : 0);
@@ -530,21 +492,22 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
         sh.keys[1] = K1;
       }
     }
-  } else {  // iterative extraction of the k+1 best keys over the register-held keys
+  } else {  // iterative extraction of the k+1 best keys
     uint64_t prev = ~(uint64_t)0;
     for (int t = 0; t <= k; ++t) {
       uint64_t best = 0;
 #pragma unroll
-      for (int i = 0; i < kSelPer; ++i)
-        if (tid + 256 * i < nb) {
-          const uint64_t c = key_of(i);
-          if (c < prev && c > best) best = c;
-        }
+      for (int i = 0; i < kSelPer; ++i) {
+        const int j = tid + 256 * i;
+        if (j >= nb) break;
+        const uint64_t c = ckey(i);
+        if (c < prev && c > best) best = c;
+      }
       best = wave_max_u64(best);
-      if (lane == 0) sh.wave_theta[w] = best;
+      if (lane == 0) sh.cand[w] = best;
       __syncthreads();
-      best = sh.wave_theta[0];
-      for (int q4 = 1; q4 < 4; ++q4) best = sh.wave_theta[q4] > best ? sh.wave_theta[q4] : best;
+      best = sh.cand[0];
+      for (int q4 = 1; q4 < 4; ++q4) best = sh.cand[q4] > best ? sh.cand[q4] : best;
       if (tid == 0) {
         if (t == k - 1) sh.keys[0] = best;
         sh.keys[1] = best;
@@ -557,30 +520,29 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   const uint64_t Kk = sh.keys[0], K1 = sh.keys[1];
 
   // 2. certification
-  int mode = 0;  // 0: select by key (exact scores); 1: score >= lo; 2: > hi or rescored
+  int mode = 0;  // 0: by key (exact scores); 1: score >= lo; 2: score > hi, or rescored
   double lo = 0.0, hi = 0.0;
   if (dmax > 0.f) {
     lo = (double)unord_f32((uint32_t)(Kk >> 32)) - 2.0 * (double)dmax;
     hi = (double)unord_f32((uint32_t)(K1 >> 32)) + 2.0 * (double)dmax;
-    int nin = 0;
+    int nin = 0, nbd = 0;
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i)
-      if (tid + 256 * i < nb) {
-        const double s_ = (double)sv[i];
-        if (s_ > hi) {
-          ++nin;
-        } else if (s_ >= lo) {
-          const int slot = atomicAdd(&sh.counters[2], 1);
-          if (slot < kBandCap) {
-            sh.band[slot] = tid + 256 * i;
-            sh.dots[slot] = -INFINITY;
-          }
-        }
-      }
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = tid + 256 * i;
+      if (j >= nb) break;
+      const double s_ = (double)sv[i];
+      nin += s_ > hi;
+      nbd += (s_ >= lo && !(s_ > hi));
+    }
     nin = lane_sum<1, 64>(nin);
-    if (lane == 0) atomicAdd(&sh.counters[1], nin);
+    nbd = lane_sum<1, 64>(nbd);
+    if (lane == 0) {
+      sh.wsum[w] = nin;
+      sh.wsum[4 + w] = nbd;
+    }
     __syncthreads();
-    const int nband = sh.counters[2], need = k - sh.counters[1];
+    const int need = k - (sh.wsum[0] + sh.wsum[1] + sh.wsum[2] + sh.wsum[3]);
+    const int nband = sh.wsum[4] + sh.wsum[5] + sh.wsum[6] + sh.wsum[7];
     if (nband == need) {
       mode = 1;
     } else if (nband > kBandCap) {
@@ -588,21 +550,33 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       mode = 0;
     } else {
       mode = 2;
-      // exact rescore: work item = (band block, token, half of the dims); each
-      // thread loads up to four items before computing any of them
+#pragma unroll
+      for (int i = 0; i < kSelPer; ++i) {
+        const int j = tid + 256 * i;
+        if (j >= nb) break;
+        const double s_ = (double)sv[i];
+        if (s_ >= lo && !(s_ > hi)) {
+          const int slot = atomicAdd(&sh.cnt[2], 1);
+          sh.band[slot] = j;
+          sh.dots[slot] = -INFINITY;
+        }
+      }
+      __syncthreads();
+      // exact rescore: thread (t, h) takes token t, dims [64 h, 64 h + 64) of up
+      // to four band blocks per batch, loading all four before computing
       bool inexact = false;
       constexpr int kBatch = 4;
+      const int t = tid >> 1, h = tid & 1;
       for (int m0 = 0; m0 < nband; m0 += kBatch) {
         u32x4 w0[kBatch], w1[kBatch];
         uint32_t sb4[kBatch];
         int pg[kBatch];
-        const int t = tid >> 1, h = tid & 1;
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int m = m0 + u;
           pg[u] = -1;
           if (m < nband) {
-            const int page = sh.bt[sh.band[m]];
+            const int page = a.block_table[(int64_t)b * a.bt_stride + sh.band[m]];
             if (page >= 0 && page < a.num_pages) {
               pg[u] = page;
               const uint8_t* pp = a.idx_data + (int64_t)page * (kPage * kPayload) + t * kPayload + 32 * h;
@@ -616,7 +590,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const int m = m0 + u;
-          if (m >= nband) break;  // uniform
+          if (m >= nband) break;
           const int j = sh.band[m];
           double acc = 0.0, mag = 0.0;
           int lk = INT_MAX;
@@ -636,7 +610,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
                 svd[g] = __builtin_ldexp(1.0, (int)byte - 127);
                 lsb = (int)byte - 127;
               }
-              if (lsb != INT_MAX) lk = min(lk, lsb - 1);
+              if (lsb != INT_MAX) lk = min(lk, lsb - 1);  // codes are multiples of 1/2
             }
 #pragma unroll
             for (int wi = 0; wi < 8; ++wi) {
@@ -650,7 +624,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
                   case 2: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); pr = make_float2(x[0], x[1]); break; }
                   default: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); pr = make_float2(x[0], x[1]); break; }
                 }
-                const int dd = 8 * wi + 2 * bs;  // dim within the half
+                const int dd = 8 * wi + 2 * bs;
                 const double s_ = svd[FMT == 1 ? (dd >> 4) : (dd >> 5)];
                 const double k0 = (double)pr.x * s_, k1 = (double)pr.y * s_;
                 const double q0 = sh.q[64 * h + dd], q1 = sh.q[64 * h + dd + 1];
@@ -661,21 +635,19 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
               }
             }
           }
-          // the two halves of a token sit in lanes 2u, 2u + 1
-          acc += lane_xor<1>(acc);
+          acc += lane_xor<1>(acc);  // the two halves of a token sit in lanes 2u, 2u + 1
           mag += lane_xor<1>(mag);
           lk = min(lk, lane_xor<1>(lk));
           const bool valid = pg[u] >= 0 && (j * kPage + t < len);
           if (valid && mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
             inexact = true;
           double v = valid ? acc + 0.0 : -INFINITY;
-          v = lane_reduce<1, 64>(v, [](double x, double y) { return fmax(x, y); });  // 32 tokens of block m
+          v = lane_reduce<1, 64>(v, [](double x, double y) { return fmax(x, y); });
           if (lane == 0) lds_max_f64(&sh.dots[m], v);
         }
       }
       if (inexact) set_status(a.status, kDevInexact);
       __syncthreads();
-      // fill the open slots by (exact score, tie-rule id)
       for (int i = tid; i < nband; i += 256) {
         const double ei = sh.dots[i] + 0.0;
         const int ji = sh.band[i];
@@ -687,30 +659,33 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
           const uint32_t km = th ? (uint32_t)jm : ~(uint32_t)jm;
           rank += (em > ei) || (em == ei && km > ki);
         }
-        if (rank < need) atomicOr(&sh.bits[ji >> 5], 1u << (ji & 31));
+        if (rank < need) atomicOr(reinterpret_cast<unsigned long long*>(&sh.sel[ji >> 6]), 1ull << (ji & 63));
       }
+      __syncthreads();
     }
   }
-  // 3. selection bitmap, then ascending emission by wave 0
+  // 3. selection bitmap: word 4 i + w holds blocks 256 i + 64 w .. + 63
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
+    if (256 * i >= nb) break;  // uniform
     const int j = tid + 256 * i;
+    bool sel = false;
     if (j < nb) {
-      bool sel;
-      if (mode == 0) sel = key_of(i) >= Kk;
+      if (mode == 0) sel = ckey(i) >= Kk;
       else if (mode == 1) sel = (double)sv[i] >= lo;
       else sel = (double)sv[i] > hi;
-      if (sel) atomicOr(&sh.bits[j >> 5], 1u << (j & 31));
     }
+    const uint64_t m = __ballot(sel);
+    if (lane == 0 && 256 * i + 64 * w < nb) sh.sel[4 * i + w] |= m;
   }
   __syncthreads();
   if (w != 0) return;
   int pos = 0;
-  const int nwords = (nb + 31) / 32;
+  const int nwords = (nb + 63) / 64;
   for (int w0 = 0; w0 < nwords; w0 += 64) {
     const int wi = w0 + lane;
-    const uint32_t word = wi < nwords ? sh.bits[wi] : 0u;
-    const int c = __popc(word);
+    const uint64_t word = wi < nwords ? sh.sel[wi] : 0ull;
+    const int c = __popcll(word);
     int incl = c;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -718,11 +693,11 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       if (lane >= off) incl += y;
     }
     int p = pos + incl - c;
-    uint32_t m = word;
+    uint64_t m = word;
     while (m) {
-      const int bit = __builtin_ctz(m);
+      const int bit = __builtin_ctzll(m);
       m &= m - 1;
-      if (p < k) out[p] = 32 * wi + bit;
+      if (p < k) out[p] = 64 * wi + bit;
       ++p;
     }
     pos += __shfl(incl, 63, 64);

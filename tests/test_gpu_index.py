@@ -115,3 +115,31 @@ def test_index_bad_page_is_flagged(gpu):
     torch.cuda.synchronize()
     assert int(st.item()) & gpu.DEV_BITS["BAD_PAGE"]
     assert 5 not in ids.cpu().numpy()[0].tolist()
+
+
+@pytest.mark.parametrize("topk", [16, 63, 64])
+def test_index_wave_boundaries(gpu, topk):
+    # block counts around the select's 64-per-wave and 256-per-pass boundaries
+    seq = [64 * 128 * 3 + 1, 195 * 128, 256 * 128, 257 * 128 + 7, 40000]
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=seq, q_len=2, G=2, topk=topk)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, "nvfp4", topk)
+
+
+
+@pytest.mark.parametrize("fill", [0x7F, 0xFF])
+def test_index_dirty_workspace(gpu, fill):
+    """Workspace entries of blocks past a row's causal range are never written by the
+    scan; the select must not read them (a stale huge or NaN bound would widen the
+    certification band). The workspace is filled with junk bytes before the call."""
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=[9000, 700, 30000], q_len=3, G=2, topk=16)
+    lay = step.case.layout
+    ws = gpu.index_workspace(step.rows, lay.max_blocks, 16, DEV)
+    ws.fill_(fill)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids = gpu.m3s_index_topk(step.cache, step.case.q_idx, torch.as_tensor(lay.block_table, device=DEV),
+                             lay.max_blocks, step.rows, 16, workspace=ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0, hex(int(st.item()))
+    assert torch.equal(ids, step.ids)
+    _check_all(gpu, step, "nvfp4", 16)
