@@ -105,6 +105,71 @@ def cpu_baseline(cfg, case, nreq, log_fn):
                       f"sort top-k, float64 softmax attention), history quantization untimed; {dt:.1f} s"}
 
 
+COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
+
+
+def _pmc_per_dispatch(path, counter):
+    """Average counter value (KiB) per dispatch, by kernel name, from a rocprofv3 counter CSV."""
+    import csv
+    acc = {}
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter:
+                continue
+            key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (name, _), v in acc.items():
+        per.setdefault(name, []).append(v)
+    return {n: (sum(v) / len(v), len(v)) for n, v in per.items()}
+
+
+def ingest_pmc(fetch_csv, write_csv, config):
+    """HBM bytes per m3s_index_topk launch, from FETCH_SIZE / WRITE_SIZE counters scaled by
+    what the same counters read for the calibration copy (COPY_BYTES read + COPY_BYTES
+    written)."""
+    import workloads as W
+    cfg = W.config(int(config) if config.isdigit() else config)
+    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        hits = [(n, v) for n, v in d.items() if key in n]
+        if not hits:
+            raise SystemExit(f"no kernel matching {key!r} in the counter file")
+        return max(hits, key=lambda t: t[1][1])[1]
+
+    copy_f, _ = pick(fetch, "neg")
+    copy_w, _ = pick(write, "neg")
+    f_scale = COPY_BYTES / (copy_f * 1024.0)
+    w_scale = COPY_BYTES / (copy_w * 1024.0)
+    parts = {}
+    for k in ("index_scan_kernel", "index_select_kernel"):
+        fk, nf = pick(fetch, k)
+        wk, nw = pick(write, k)
+        parts[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "dispatches": [nf, nw],
+                    "fetch_bytes": round(fk * 1024.0 * f_scale), "write_bytes": round(wk * 1024.0 * w_scale)}
+    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in parts.values())
+    rec = {"workload": cfg.name, "source_sha": source_sha(INDEX_SOURCES), "bytes_per_launch": total,
+           "kernels": parts,
+           "calibration": {"copy_bytes_each_way": COPY_BYTES, "copy_fetch_kib": round(copy_f, 1),
+                           "copy_write_kib": round(copy_w, 1), "fetch_scale": round(f_scale, 4),
+                           "write_scale": round(w_scale, 4)},
+           "commands": ["cd /tmp && export TMPDIR=/tmp  # $R = repository root",
+                        *[f"timeout -s KILL 150 rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/pmc_{d} "
+                          f"-o run -- python -u $R/bench.py --config {cfg.name} --steps 5 --warmup 2 "
+                          f"--stage-reps 10 --no-cpu --copy-calibration" for c, d in (("FETCH_SIZE", "fetch"),
+                                                                                     ("WRITE_SIZE", "write"))],
+                        f"python bench.py --config {cfg.name} --ingest-pmc "
+                        f"gpurun_out/pmc_fetch/run_counter_collection.csv "
+                        f"gpurun_out/pmc_write/run_counter_collection.csv"]}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    log(json.dumps(rec, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,7 +180,16 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB float32 copy kernel (torch.neg) whose HBM bytes are known, "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE run, "
+                         "WRITE_SIZE run) of 'bench.py --copy-calibration' into the traffic record")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.config)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only: the path is one GPU's share (one KV head, one TP rank); "
@@ -208,6 +282,15 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; {NL} layers x {lay.num_pages} pages; "
         f"rows {R}, G {G}, top-k {cfg.topk}")
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy: {COPY_BYTES >> 20} MiB read + written, 3 launches")
 
     # ---- timed region: K steps, graph replays cycling over the layers
     for i in range(args.warmup):
