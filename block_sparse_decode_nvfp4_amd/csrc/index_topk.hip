@@ -82,11 +82,115 @@ __device__ __forceinline__ void load_page(PageBuf& p, const IndexArgs& a, int pa
 }
 
 // Per-request query state of a wave (rows r0 .. r0 + ql - 1 of request b).
+// NVFP4: op = the row's 2^P-scaled fp16 query (B operand of the f16 MFMA).
+// MXFP4: qb[t] / qsc[t] = term t of the query as e4m3 bytes with its E8M0 scale
+// (B operand of the scaled fp4 MFMA).
 struct QueryTile {
   f16x8 op[4];
+  i32x8 qb[3];
+  int qsc[3];
   float qs0, qs1, qe0, qe1, unscale;
   int b, r0, ql, len_n, min_len;
 };
+
+// MXFP4 query: the B operand of v_mfma_scale_f32_16x16x128_f8f6f4 in e4m3 holds, in
+// lane (n, G), column (row) n with dims [16 G, 16 G + 16) in bytes 0-15 and
+// [64 + 16 G, 64 + 16 G + 16) in bytes 16-31; the lane's scale is that of row n,
+// dims [32 G, 32 G + 32) (layout measured on gfx950). Each 32-dim block of the
+// bf16 row, with largest magnitude in [2^e, 2^(e+1)), is written as
+//   q = 2^s1 t1 + 2^s2 t2 + 2^s3 t3 + r,  s1 = e - 3, s2 = s1 - 5, s3 = s2 - 5,
+// each t an integer in [-16, 16] (exact in e4m3) taken by round-to-nearest of
+// what the earlier terms leave, and r the exact remainder (|r| <= 2^(s3 - 1)).
+// With integer-valued e4m3 operands the scaled MFMA accumulates like fp32 (its
+// error on full-range e4m3 operands is far larger, which this split avoids).
+// qs0 = sum over the lane's scale block of |2^s t| over the three terms and
+// qe0 = sum of |r|: the scorer's error bound is 6 smax (2^-15 qs0 + qe0) per
+// block, the 2^-15 covering any order of the <= 383 fp32 additions of the three
+// chained MFMAs (383 * 2^-24 < 2^-15).
+__device__ __forceinline__ void load_query_mx(QueryTile& q, const IndexArgs& a, int n, int G) {
+  u32x4 raw[4] = {};
+  if (n < q.ql) {
+    const uint16_t* qp = a.q_idx + (int64_t)(q.r0 + n) * a.q_stride;
+    raw[0] = *reinterpret_cast<const u32x4*>(qp + 16 * G);
+    raw[1] = *reinterpret_cast<const u32x4*>(qp + 16 * G + 8);
+    raw[2] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G);
+    raw[3] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G + 8);
+  }
+  // half 0 (raw[0..1]) lies in block G / 2, half 1 (raw[2..3]) in block 2 + G / 2;
+  // lanes G and G ^ 1 hold the two halves of each block
+  uint32_t mh[2] = {0u, 0u};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mh[s >> 1] = max(mh[s >> 1], max(raw[s][w] & 0x7FFFu, (raw[s][w] >> 16) & 0x7FFFu));
+  int s1h[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t m = max(mh[h], lane_xor<16>(mh[h]));
+    s1h[h] = m ? max(bf16_floor_log2(m) - 3, -127) : 0;
+  }
+  float qabs[2] = {0.f, 0.f}, qres[2] = {0.f, 0.f};
+  int words[2][4][3];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int h = s >> 1;
+    const int sc1 = s1h[h], sc2 = max(sc1 - 5, -127), sc3 = max(sc2 - 5, -127);
+#pragma unroll
+    for (int w = 0; w < 4; w += 2) {
+      float t[3][4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t word = raw[s][w + (e >> 1)];
+        float x = bf16_bits_to_f32((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+        const float t1 = __builtin_rintf(__builtin_ldexpf(x, -sc1));
+        x -= __builtin_ldexpf(t1, sc1);
+        const float t2 = __builtin_rintf(__builtin_ldexpf(x, -sc2));
+        x -= __builtin_ldexpf(t2, sc2);
+        const float t3 = __builtin_rintf(__builtin_ldexpf(x, -sc3));
+        x -= __builtin_ldexpf(t3, sc3);
+        t[0][e] = t1;
+        t[1][e] = t2;
+        t[2][e] = t3;
+        qabs[h] += __builtin_ldexpf(fabsf(t1), sc1) + __builtin_ldexpf(fabsf(t2), sc2) + __builtin_ldexpf(fabsf(t3), sc3);
+        qres[h] += fabsf(x);
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        int v = __builtin_amdgcn_cvt_pk_fp8_f32(t[k][0], t[k][1], 0, false);
+        v = __builtin_amdgcn_cvt_pk_fp8_f32(t[k][2], t[k][3], v, true);
+        words[h][(s & 1) * 2 + (w >> 1)][k] = v;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      q.qb[k][d] = words[0][d][k];
+      q.qb[k][4 + d] = words[1][d][k];
+    }
+  }
+  // the lane supplies the scale (and takes the bound sums) of block G: block G < 2
+  // is half 0 of lanes 2G, 2G + 1; block G >= 2 is half 1 of lanes 2G - 4, 2G - 3
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qabs[h] += lane_xor<16>(qabs[h]);
+    qres[h] += lane_xor<16>(qres[h]);
+  }
+  const int src = n + 16 * ((2 * G) & 3);
+  const int e0 = __shfl(s1h[0], src, 64), e1 = __shfl(s1h[1], src, 64);
+  const float a0 = __shfl(qabs[0], src, 64), a1 = __shfl(qabs[1], src, 64);
+  const float r0 = __shfl(qres[0], src, 64), r1 = __shfl(qres[1], src, 64);
+  const int sc1 = G < 2 ? e0 : e1;
+  const int sc2 = max(sc1 - 5, -127), sc3 = max(sc2 - 5, -127);
+  q.qsc[0] = sc1 + 127;
+  q.qsc[1] = sc2 + 127;
+  q.qsc[2] = sc3 + 127;
+  q.qs0 = G < 2 ? a0 : a1;
+  q.qe0 = G < 2 ? r0 : r1;
+  q.qs1 = q.qe1 = 0.f;
+  q.unscale = 1.0f;
+}
 
 template <int FMT>
 __device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int n, int G) {
@@ -95,6 +199,10 @@ __device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int
   q.ql = a.cu_q[b + 1] - q.r0;
   q.min_len = a.row_len[q.r0];
   q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
+  if (FMT == 2) {
+    load_query_mx(q, a, n, G);
+    return;
+  }
   u32x4 raw[4] = {};
   if (n < q.ql) {
     const uint16_t* qp = a.q_idx + (int64_t)(q.r0 + n) * a.q_stride + 32 * G;
@@ -149,10 +257,12 @@ __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q,
       acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][2]) * s1, q.op[2], acc);
       acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][3]) * s1, q.op[3], acc);
     } else {
-      const float s = e8m0_to_f32(p.ks[i]);
-      smx_mx = fmaxf(smx_mx, s);
+      // the lane's 32 codes and E8M0 byte are the fp4 A operand and its scale as loaded
+      smx_mx = fmaxf(smx_mx, e8m0_to_f32(p.ks[i]));
+      const i32x8 ka = {(int)p.kr[i][0], (int)p.kr[i][1], (int)p.kr[i][2], (int)p.kr[i][3], 0, 0, 0, 0};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc = mfma_f16(fp4x8_to_f16_pow2(p.kr[i][t], s), q.op[t], acc);
+      for (int t = 0; t < 3; ++t)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q.qb[t], acc, 4, 0, 0, (int)p.ks[i], 0, q.qsc[t]);
     }
     if (need_mask) {
       const int t0 = j * kPage + 16 * i + 4 * G;

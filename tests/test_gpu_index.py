@@ -143,3 +143,37 @@ def test_index_dirty_workspace(gpu, fill):
     assert int(st.item()) == 0, hex(int(st.item()))
     assert torch.equal(ids, step.ids)
     _check_all(gpu, step, "nvfp4", 16)
+
+
+def _adversarial_queries(R, seed):
+    """Index queries whose 32-dim blocks stress the scorers' query handling: an all-zero
+    block, blocks spanning 24 binades, one dominant element over tiny ones, values whose
+    quotient by the block's leading power rounds to 16, and exact powers of two."""
+    g = np.random.default_rng(seed)
+    q = g.standard_normal((R, 128)) / np.sqrt(128.0)
+    for r in range(R):
+        kind = r % 4
+        if kind == 0:
+            q[r, 0:32] = 0.0
+            e = -(np.arange(32) % 25)
+            q[r, 32:64] = np.where(np.arange(32) % 2, -1.0, 1.0) * np.ldexp(1.0 + (np.arange(32) % 7) / 8.0, e)
+        elif kind == 1:
+            q[r, 64:96] = np.ldexp(1.0, -18) * g.standard_normal(32)
+            q[r, 64] = 8.0
+            q[r, 96:128] = np.ldexp(1.0 + 127.0 / 128.0, -3) * np.sign(g.standard_normal(32))
+        elif kind == 2:
+            q[r, :] = np.ldexp(1.0, g.integers(-12, 2, 128)) * np.sign(g.standard_normal(128))
+        else:
+            q[r, 0:32] = np.ldexp(1.0 + 1.0 / 2 + 1.0 / 16 + 1.0 / 128, -4) * np.sign(g.standard_normal(32))
+            q[r, 32:64] *= 2.0 ** 20
+    return torch.as_tensor(q, dtype=torch.float32).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_index_adversarial_queries(gpu, fmt):
+    seq = [6000, 128 * 20 + 3, 2500]
+    case = W.make_case(CFG0, DEV, seq_lens=seq, q_len=4, G=2)
+    qi = _adversarial_queries(case.q_idx.shape[0], 11).to(DEV)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=8, case=case, fmt=fmt, q_idx=qi)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, fmt, 8)
