@@ -6,6 +6,8 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <atomic>
+
 #include "m3s.h"
 #include "launch.hpp"
 
@@ -41,14 +43,19 @@ m3s_status check_table(const int32_t* bt, int32_t bt_stride, int32_t max_blocks)
 }
 
 int scan_grid() {
-  static int cached = 0;
-  if (cached) return cached;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  cached = 2 * cus;  // the scan kernel keeps 2 workgroups (8 waves) resident per CU
-  return cached;
+  // one 8-wave scan workgroup per CU of the current device
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  std::atomic<int>* slot = (dev >= 0 && dev < 64) ? &cached[dev] : nullptr;
+  if (slot) {
+    const int c = slot->load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (slot) slot->store(cus, std::memory_order_relaxed);
+  return cus;
 }
 
 m3s_status from_hip(hipError_t e) { return e == hipSuccess ? M3S_OK : M3S_ERR_HIP; }

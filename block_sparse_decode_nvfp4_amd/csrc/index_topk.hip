@@ -291,23 +291,29 @@ __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q,
 }
 
 // Streaming scan. The (request, block) units of all requests form one flat list
-// (block fastest); wave w of the grid takes the contiguous slice
-// [w * N / W, (w + 1) * N / W). The block-table entries of a wave's units are
-// fetched lane-parallel up front, and each page's loads are issued one unit
-// ahead of its scoring, so every wave keeps about two pages in flight.
+// (block fastest). Workgroup g (8 waves, one per CU) takes the contiguous slice
+// [g * N / W, (g + 1) * N / W), so consecutive slices of a long request land on
+// different XCDs. The slice's block-table entries are staged in LDS, and its
+// waves claim units one at a time from an LDS counter: a wave whose pages arrive
+// late simply takes fewer units, so the waves of a workgroup finish together.
+// Each wave keeps two pages in flight (one scoring, one loading).
+constexpr int kScanWaves = 8;
+constexpr int kScanChunk = 1024;  // units staged in LDS at a time
+
 template <int FMT>
-__global__ __launch_bounds__(256) void index_scan_kernel(IndexArgs a) {
+__global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a) {
   __shared__ int s_blk[M3S_MAX_REQS_INTERNAL + 1];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __shared__ int s_unit[kScanChunk];  // request * kMaxBlocks + block; -1: not scored
+  __shared__ int s_page[kScanChunk];  // page; -1: unusable
+  __shared__ int s_ctr;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, G = lane >> 4;
   const int B = a.num_reqs;
-  for (int i = threadIdx.x; i <= B; i += 256) s_blk[i] = a.req_blk[i];
+  for (int i = tid; i <= B; i += kScanWaves * 64) s_blk[i] = a.req_blk[i];
   __syncthreads();
   const int64_t total = s_blk[B];
-  const int64_t nw = (int64_t)gridDim.x * 4;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + wid;
-  const int64_t u0 = gw * total / nw, u1 = (gw + 1) * total / nw;
-  if (u0 >= u1) return;  // no barrier follows
+  const int64_t w0 = (int64_t)blockIdx.x * total / gridDim.x;
+  const int64_t w1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
 
   auto req_of = [&](int64_t u) {  // largest b with s_blk[b] <= u
     int lo = 0, hi = B - 1;
@@ -317,67 +323,68 @@ __global__ __launch_bounds__(256) void index_scan_kernel(IndexArgs a) {
     }
     return lo;
   };
+  auto claim = [&]() {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_ctr, 1);
+    return __builtin_amdgcn_readlane(v, 0);
+  };
 
   QueryTile qt;
   qt.b = -1;
   PageBuf pa, pb;
-  int b = req_of(u0);
-  for (int64_t c0 = u0; c0 < u1; c0 += 64) {
-    const int cnt = (int)min((int64_t)64, u1 - c0);
-    // lane i: page of unit c0 + i (-1 when unusable)
-    int my_page = -1;
-    if (lane < cnt) {
-      const int64_t u = c0 + lane;
+  auto process = [&](const PageBuf& buf, int i) {
+    const int key = s_unit[i];
+    if (key < 0) return;
+    const int bb = key / kMaxBlocks, j = key - bb * kMaxBlocks;
+    if (bb != qt.b) load_query<FMT>(qt, a, bb, n, G);
+    if (s_page[i] >= 0) {
+      score_page<FMT>(buf, qt, a, j, n, G);
+    } else if (G == 0 && n < qt.ql) {
+      const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + j;
+      a.ws_score[o] = -INFINITY;
+      a.ws_bound[o] = 0.f;
+    }
+  };
+
+  for (int64_t c0 = w0; c0 < w1; c0 += kScanChunk) {  // uniform over the workgroup
+    const int cnt = (int)min((int64_t)kScanChunk, w1 - c0);
+    for (int i = tid; i < cnt; i += kScanWaves * 64) {
+      const int64_t u = c0 + i;
       const int bl = req_of(u);
       const int jl = (int)(u - s_blk[bl]);
+      int key = -1, pg = -1;
       if (jl < a.max_blocks) {
-        const int pg = a.block_table[(int64_t)bl * a.bt_stride + jl];
-        my_page = (pg >= 0 && pg < a.num_pages) ? pg : -1;
-        if (my_page < 0) set_status(a.status, kDevBadPage);
+        key = bl * kMaxBlocks + jl;
+        pg = a.block_table[(int64_t)bl * a.bt_stride + jl];
+        if (pg < 0 || pg >= a.num_pages) {
+          set_status(a.status, kDevBadPage);
+          pg = -1;
+        }
       } else {
         set_status(a.status, kDevBadLength);
       }
+      s_unit[i] = key;
+      s_page[i] = pg;
     }
-    int pg0 = __builtin_amdgcn_readlane(my_page, 0);
-    if (pg0 >= 0) load_page<FMT>(pa, a, pg0, n, G);
-    for (int i = 0; i < cnt; i += 2) {
-      // unit c0 + i is in pa; issue c0 + i + 1 into pb
-      const int pg1 = i + 1 < cnt ? __builtin_amdgcn_readlane(my_page, i + 1) : -1;
-      if (pg1 >= 0) load_page<FMT>(pb, a, pg1, n, G);
-      {
-        const int64_t u = c0 + i;
-        while (b + 1 < B && u >= s_blk[b + 1]) ++b;
-        const int j = (int)(u - s_blk[b]);
-        if (j < a.max_blocks) {
-          if (b != qt.b) load_query<FMT>(qt, a, b, n, G);
-          if (pg0 >= 0) {
-            score_page<FMT>(pa, qt, a, j, n, G);
-          } else if (G == 0 && n < qt.ql) {
-            const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + j;
-            a.ws_score[o] = -INFINITY;
-            a.ws_bound[o] = 0.f;
-          }
-        }
-      }
-      if (i + 1 >= cnt) break;
-      pg0 = i + 2 < cnt ? __builtin_amdgcn_readlane(my_page, i + 2) : -1;
-      if (pg0 >= 0) load_page<FMT>(pa, a, pg0, n, G);
-      {
-        const int64_t u = c0 + i + 1;
-        while (b + 1 < B && u >= s_blk[b + 1]) ++b;
-        const int j = (int)(u - s_blk[b]);
-        if (j < a.max_blocks) {
-          if (b != qt.b) load_query<FMT>(qt, a, b, n, G);
-          if (pg1 >= 0) {
-            score_page<FMT>(pb, qt, a, j, n, G);
-          } else if (G == 0 && n < qt.ql) {
-            const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + j;
-            a.ws_score[o] = -INFINITY;
-            a.ws_bound[o] = 0.f;
-          }
-        }
-      }
+    if (tid == 0) s_ctr = 0;
+    __syncthreads();
+    // claims of a wave increase, so the units are scored in claim order and the
+    // first claim past the chunk ends the wave's work on it
+    int i0 = claim();
+    if (i0 < cnt && s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
+    int i1 = claim();
+    if (i1 < cnt && s_page[i1] >= 0) load_page<FMT>(pb, a, s_page[i1], n, G);
+    while (true) {
+      if (i0 >= cnt) break;
+      process(pa, i0);
+      i0 = claim();
+      if (i0 < cnt && s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
+      if (i1 >= cnt) break;
+      process(pb, i1);
+      i1 = claim();
+      if (i1 < cnt && s_page[i1] >= 0) load_page<FMT>(pb, a, s_page[i1], n, G);
     }
+    __syncthreads();  // the chunk's LDS tables are rewritten next
   }
 }
 
@@ -825,13 +832,13 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   if (a.num_reqs > 0) {
     const int64_t units_upper = (int64_t)a.num_reqs * a.max_blocks;
-    int64_t grid = (units_upper + 3) / 4;
+    int64_t grid = (units_upper + kScanWaves - 1) / kScanWaves;
     if (grid > a.scan_grid) grid = a.scan_grid;
     if (grid < 1) grid = 1;
     if (a.format == 1)
-      hipLaunchKernelGGL(index_scan_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(index_scan_kernel<1>, dim3((unsigned)grid), dim3(kScanWaves * 64), 0, stream, a);
     else
-      hipLaunchKernelGGL(index_scan_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+      hipLaunchKernelGGL(index_scan_kernel<2>, dim3((unsigned)grid), dim3(kScanWaves * 64), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
