@@ -17,6 +17,9 @@
 // combine kernel - one workgroup per row merges the splits:
 //   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s (log2 domain).
 // With a single split the split kernel writes the normalized output itself.
+// (Merging in the split kernel's last workgroup instead needs a device-scope
+// release of the partials, an L2 writeback per wave on this GPU; measured, it
+// cost more than the separate launch.)
 #include <float.h>
 
 #include "fp4.hpp"
@@ -28,11 +31,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kVRow = kDim + 8;  // LDS row of one token's decoded V (fp16), padded
-constexpr int kVChunk = 32;      // tokens of V staged per step
+constexpr int kVChunk = 64;      // tokens of V staged per step (2 MFMA k-steps)
 
 struct AttendShared {
   union {
-    _Float16 v[kWaves][kVChunk][kVRow];       // 34,816 B
+    _Float16 v[kWaves][kVChunk][kVRow];       // 69,632 B
     struct {
       float o[kWaves][16][kDim];              // 32,768 B
       float m[kWaves][16];
@@ -58,12 +61,19 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
   const int sp = blockIdx.x - r * a.nsplit;
   const int slot = sp * kWaves + w;
 
-  // ---- which block this wave attends
+  // ---- which block this wave attends; the row map, the id and the query are
+  // independent loads, issued together
   const int b = a.row_req[r];
   const int len = a.row_len[r];
+  const int id = slot < a.topk ? a.topk_ids[(int64_t)r * a.topk + slot] : -1;
+  u32x4 raw[4] = {};
+  if (n < a.num_heads) {
+    const uint16_t* qp = a.q + (int64_t)r * a.q_row_stride + (int64_t)n * a.q_head_stride + 32 * G;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+  }
   int page = -1, blk = -1;
   if (b >= 0 && len > 0 && slot < a.topk) {
-    const int id = a.topk_ids[(int64_t)r * a.topk + slot];
     const int nbr = (len + kPage - 1) / kPage;
     if (id >= 0) {
       if (id >= nbr || id >= a.max_blocks) {
@@ -114,12 +124,6 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
     }
 
     // ---- query heads as the B operand, scaled by 2^P into fp16 range
-    u32x4 raw[4] = {};
-    if (n < a.num_heads) {
-      const uint16_t* qp = a.q + (int64_t)r * a.q_row_stride + (int64_t)n * a.q_head_stride + 32 * G;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
-    }
     uint32_t mx = 0;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -181,17 +185,17 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
     lsum = lane_sum<16, 64>(lsum);
     l_run = lsum;
 
-    // ---- O += P V, 32 tokens (tiles 2c, 2c+1) per step
+    // ---- O += P V, 64 tokens (tiles 4c .. 4c+3) staged per step, 32 per MFMA
     _Float16(*vb)[kVRow] = sh.v[w];
 #pragma unroll
-    for (int cidx = 0; cidx < 4; ++cidx) {
+    for (int cidx = 0; cidx < kPage / kVChunk; ++cidx) {
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int i = 2 * cidx + h2;
+      for (int h4 = 0; h4 < kVChunk / 16; ++h4) {
+        const int i = (kVChunk / 16) * cidx + h4;
         typename Dec::scale_t s0, s1;
         if (FMT == 1) { s0 = Dec::scale(vs[i] & 0xFFu); s1 = Dec::scale(vs[i] >> 8); }
         else { s0 = s1 = Dec::scale(vs[i]); }
-        _Float16* dst = &vb[16 * h2 + n][32 * G];
+        _Float16* dst = &vb[16 * h4 + n][32 * G];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           *reinterpret_cast<f16x8*>(dst + 8 * s) = Dec::run(vr[i][s], s < 2 ? s0 : s1);
@@ -199,23 +203,28 @@ __global__ __launch_bounds__(256) void attend_split_kernel(AttendArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // A operand: head n, tokens {4G..4G+3} of tile 2c then of tile 2c+1
-      f16x8 pa;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        pa[v] = (_Float16)st[2 * cidx][v];
-        pa[4 + v] = (_Float16)st[2 * cidx + 1][v];
-      }
-      // B operand for N tile t: V[those 8 tokens][16 t + n]; lane n of a 16-lane
-      // group points at token (4G + n / 4), dims 16 t + 4 (n % 4) .. + 3.
+      for (int ks = 0; ks < kVChunk / 32; ++ks) {
+        const int i0 = (kVChunk / 16) * cidx + 2 * ks;
+        // A operand: head n, tokens {4G..4G+3} of tile i0 then of tile i0 + 1
+        f16x8 pa;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const f16x4 lo = lds_tr16(&vb[4 * G + (n >> 2)][16 * t + 4 * (n & 3)]);
-        const f16x4 hi = lds_tr16(&vb[16 + 4 * G + (n >> 2)][16 * t + 4 * (n & 3)]);
-        f16x8 bv;
-        bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
-        bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
-        o[t] = mfma_f16(pa, bv, o[t]);
+        for (int v = 0; v < 4; ++v) {
+          pa[v] = (_Float16)st[i0][v];
+          pa[4 + v] = (_Float16)st[i0 + 1][v];
+        }
+        // B operand for N tile t: V[those 8 tokens][16 t + n]; lane n of a 16-lane
+        // group points at token (4G + n / 4), dims 16 t + 4 (n % 4) .. + 3.
+        const int r0 = 32 * ks + 4 * G + (n >> 2);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const f16x4 lo = lds_tr16(&vb[r0][16 * t + 4 * (n & 3)]);
+          const f16x4 hi = lds_tr16(&vb[r0 + 16][16 * t + 4 * (n & 3)]);
+          f16x8 bv;
+          bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
+          bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
+          o[t] = mfma_f16(pa, bv, o[t]);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();

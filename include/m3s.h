@@ -222,9 +222,13 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
  *   topk_ids     int32 [num_rows, topk]
  *   out          fp32 [num_rows, num_heads, 128], contiguous
  *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_SPARSE_ATTEND, ...)
- * Computation: K and V are decoded exactly (bf16 / fp16), QK^T on bf16 MFMA
- * with fp32 accumulation, online softmax in fp32, PV on fp16 MFMA; split-K
- * partials are merged by a combine pass.
+ *                (split partials; none needed when topk <= 4). Calls that share
+ *                a workspace must not overlap in time.
+ * Computation: K and V are decoded exactly to fp16 (code * scale), the query is
+ * scaled by a power of two into fp16 range, QK^T and PV run on fp16 MFMA with
+ * fp32 accumulation, softmax in fp32. Each workgroup takes 4 of a row's blocks
+ * (a split); a combine pass merges the splits' partials (split-K online
+ * softmax).
  */
 m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t q_row_stride,
                              int64_t q_head_stride, int32_t num_heads,

@@ -105,3 +105,19 @@ def test_attend_large_scale_and_wide_query_range(gpu):
     assert st == 0
     for r, want in outs.items():
         assert max_rel_err(got[r], want) <= TOL, r
+
+
+@pytest.mark.parametrize("topk", [16, 64])
+def test_attend_workspace_reuse(gpu, topk):
+    """One workspace across repeated calls, first filled with junk: every call's output
+    equals the call on a fresh workspace bit for bit."""
+    seq = [4000, 1500, 9000]
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=seq, q_len=4, G=16, topk=topk)
+    lay = step.case.layout
+    ws = gpu.attend_workspace(step.rows, lay.max_blocks, topk, 16, DEV)
+    ws.fill_(0x7F)
+    for rep in range(3):
+        out = gpu.m3s_sparse_attend(step.cache, step.case.q, step.bt, lay.max_blocks, step.rows, step.ids,
+                                    step.case.cfg.sm_scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, step.out), rep
