@@ -428,31 +428,37 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) { return bitonic_
 
 // Select: one 256-thread workgroup per row.
 //   0. the row's scores (thread t holds blocks j = t + 256 i), its largest
-//      error bound and its query are loaded at once (the row length only masks);
+//      error bound and its query are loaded at once; the page ids of its
+//      blocks follow as soon as the row's request is known (a rescore needs
+//      them, and loading them here takes that load off its critical path);
 //   1. threshold: each wave bitonic-sorts its 64 thread maxima (ordered score
-//      bits); with c = ceil((k+1)/4), every wave holds c keys at or above its
-//      c-th largest maximum, so the smallest of the four is at or below the
-//      (k+1)-th best key overall; the keys at or above it (usually < 64) are
-//      sorted by one wave, giving the k-th and (k+1)-th keys (score, tie-rule
-//      id) exactly; an iterative extraction covers larger sets and k = 64;
-//   2. certification against the row's error bound: blocks above hi are in,
-//      below lo out, and the band between is rescored in exact float64 by all
-//      threads at once when it does not exactly fill the open slots;
-//   3. a selection bitmap (one ballot word per 64 blocks), emitted ascending.
-constexpr int kSelPer = kMaxBlocks / 256;  // score registers per thread
+//      bits); wave w contributes c_w of the k+1 keys (ceil((k+1)/4) each, moved
+//      to earlier waves when a short row leaves a later wave fewer live threads),
+//      so the smallest of the four c_w-th largest maxima lies at or below the
+//      (k+1)-th best key; the keys at or above it (usually < 64) are sorted by
+//      one wave as (score, tie-rule id), giving the k-th and (k+1)-th keys
+//      exactly; an iterative extraction covers larger sets and k = 64;
+//   2. certification against the row's error bound, in one pass: blocks above
+//      hi are in, below lo out, the band between is listed (with its pages,
+//      whose loads start at once) and rescored in exact float64 by all threads
+//      when it does not exactly fill the open slots;
+//   3. the k selected ids are gathered in LDS and one wave sorts them ascending.
+// Score registers per thread: PER = 8, 16 or 32 (rows of up to 256 PER blocks),
+// picked at launch from max_blocks; the smallest that fits keeps the kernel's
+// code small (it runs once per row on cold instruction caches).
 
 struct SelectShared {
-  uint64_t sel[kMaxBlocks / 64];
   uint64_t cand[64];
   int band[kBandCap];
+  int bpage[kBandCap];
   double dots[kBandCap];
   double q[kDim];
   uint32_t thr[4];
   float red[4];
   int ired[4];
-  int cnt[4];          // candidates, in, band
-  int wsum[8];
+  int cnt[4];  // candidates, in, band, selected
   uint64_t keys[2];
+  int sel[64];
 };
 
 __device__ __forceinline__ void lds_max_f64(double* p, double v) {
@@ -486,9 +492,10 @@ __device__ __forceinline__ uint32_t bitonic32_sizes(uint32_t x) {
   else return bitonic32_sizes<SIZE * 2>(bitonic32_steps<SIZE, SIZE / 2>(x));
 }
 
-template <int FMT>
+template <int FMT, int PER>
 __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   constexpr int SB = FMT == 1 ? 8 : 4;
+  constexpr int kSelPer = PER;
   __shared__ SelectShared sh;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = blockIdx.x;
@@ -518,6 +525,14 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     const bool all = b >= 0 && len > 0 && nb <= MB;
     if (tid < k) out[tid] = (all && tid < nb) ? tid : -1;
     return;
+  }
+  int pv[kSelPer];
+  const int32_t* btr = a.block_table + (int64_t)b * a.bt_stride;
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = tid + 256 * i;
+    if (j >= nb) break;
+    pv[i] = btr[j];
   }
   // blocks past the row's causal range were never scored: they never compete
   // and their workspace entries are not read
@@ -552,8 +567,6 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   }
   dm = lane_fmax<1, 64>(dm);
   lqv = lane_reduce<1, 64>(lqv, [](int x, int y) { return x < y ? x : y; });
-  // c_w keys taken from wave w: ceil((k+1)/4) each, moved to the earlier waves
-  // where a short row leaves a later wave fewer than that many live threads
   const bool small_k = k < 64;
   int cw = 0;
   {
@@ -581,7 +594,6 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     sh.thr[w] = theta_w;
   }
   if (tid < 4) sh.cnt[tid] = 0;
-  for (int i = tid; i < (nb + 63) / 64; i += 256) sh.sel[i] = 0ull;
   __syncthreads();
   const float dmax = fmaxf(fmaxf(sh.red[0], sh.red[1]), fmaxf(sh.red[2], sh.red[3]));
   int lq = min(min(sh.ired[0], sh.ired[1]), min(sh.ired[2], sh.ired[3]));
@@ -637,29 +649,33 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   const uint64_t Kk = sh.keys[0], K1 = sh.keys[1];
 
   // 2. certification
-  int mode = 0;  // 0: by key (exact scores); 1: score >= lo; 2: score > hi, or rescored
+  int mode = 0;  // 0: by key (exact scores); 1: score >= lo; 2: score > hi, band rescored
   double lo = 0.0, hi = 0.0;
   if (dmax > 0.f) {
     lo = (double)unord_f32((uint32_t)(Kk >> 32)) - 2.0 * (double)dmax;
     hi = (double)unord_f32((uint32_t)(K1 >> 32)) + 2.0 * (double)dmax;
-    int nin = 0, nbd = 0;
+    int nin = 0;
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
       const int j = tid + 256 * i;
       if (j >= nb) break;
       const double s_ = (double)sv[i];
-      nin += s_ > hi;
-      nbd += (s_ >= lo && !(s_ > hi));
+      if (s_ > hi) {
+        ++nin;
+      } else if (s_ >= lo) {
+        const int slot = atomicAdd(&sh.cnt[2], 1);
+        if (slot < kBandCap) {
+          sh.band[slot] = j;
+          sh.bpage[slot] = pv[i];
+          sh.dots[slot] = -INFINITY;
+        }
+      }
     }
     nin = lane_sum<1, 64>(nin);
-    nbd = lane_sum<1, 64>(nbd);
-    if (lane == 0) {
-      sh.wsum[w] = nin;
-      sh.wsum[4 + w] = nbd;
-    }
+    if (lane == 0 && nin) atomicAdd(&sh.cnt[1], nin);
     __syncthreads();
-    const int need = k - (sh.wsum[0] + sh.wsum[1] + sh.wsum[2] + sh.wsum[3]);
-    const int nband = sh.wsum[4] + sh.wsum[5] + sh.wsum[6] + sh.wsum[7];
+    const int need = k - sh.cnt[1];
+    const int nband = sh.cnt[2];
     if (nband == need) {
       mode = 1;
     } else if (nband > kBandCap) {
@@ -667,23 +683,12 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       mode = 0;
     } else {
       mode = 2;
-#pragma unroll
-      for (int i = 0; i < kSelPer; ++i) {
-        const int j = tid + 256 * i;
-        if (j >= nb) break;
-        const double s_ = (double)sv[i];
-        if (s_ >= lo && !(s_ > hi)) {
-          const int slot = atomicAdd(&sh.cnt[2], 1);
-          sh.band[slot] = j;
-          sh.dots[slot] = -INFINITY;
-        }
-      }
-      __syncthreads();
       // exact rescore: thread (t, h) takes token t, dims [64 h, 64 h + 64) of up
       // to four band blocks per batch, loading all four before computing
       bool inexact = false;
       constexpr int kBatch = 4;
       const int t = tid >> 1, h = tid & 1;
+#pragma unroll 1
       for (int m0 = 0; m0 < nband; m0 += kBatch) {
         u32x4 w0[kBatch], w1[kBatch];
         uint32_t sb4[kBatch];
@@ -693,7 +698,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
           const int m = m0 + u;
           pg[u] = -1;
           if (m < nband) {
-            const int page = a.block_table[(int64_t)b * a.bt_stride + sh.band[m]];
+            const int page = sh.bpage[m];
             if (page >= 0 && page < a.num_pages) {
               pg[u] = page;
               const uint8_t* pp = a.idx_data + (int64_t)page * (kPage * kPayload) + t * kPayload + 32 * h;
@@ -704,7 +709,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
             }
           }
         }
-#pragma unroll
+#pragma unroll 1
         for (int u = 0; u < kBatch; ++u) {
           const int m = m0 + u;
           if (m >= nband) break;
@@ -776,50 +781,33 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
           const uint32_t km = th ? (uint32_t)jm : ~(uint32_t)jm;
           rank += (em > ei) || (em == ei && km > ki);
         }
-        if (rank < need) atomicOr(reinterpret_cast<unsigned long long*>(&sh.sel[ji >> 6]), 1ull << (ji & 63));
+        if (rank < need) {
+          const int slot = atomicAdd(&sh.cnt[3], 1);
+          if (slot < 64) sh.sel[slot] = ji;
+        }
       }
-      __syncthreads();
     }
   }
-  // 3. selection bitmap: word 4 i + w holds blocks 256 i + 64 w .. + 63
+  // 3. the selected ids, gathered and sorted ascending by one wave
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    if (256 * i >= nb) break;  // uniform
     const int j = tid + 256 * i;
-    bool sel = false;
-    if (j < nb) {
-      if (mode == 0) sel = ckey(i) >= Kk;
-      else if (mode == 1) sel = (double)sv[i] >= lo;
-      else sel = (double)sv[i] > hi;
+    if (j >= nb) break;
+    bool in;
+    if (mode == 0) in = ckey(i) >= Kk;
+    else if (mode == 1) in = (double)sv[i] >= lo;
+    else in = (double)sv[i] > hi;
+    if (in) {
+      const int slot = atomicAdd(&sh.cnt[3], 1);
+      if (slot < 64) sh.sel[slot] = j;
     }
-    const uint64_t m = __ballot(sel);
-    if (lane == 0 && 256 * i + 64 * w < nb) sh.sel[4 * i + w] |= m;
   }
   __syncthreads();
   if (w != 0) return;
-  int pos = 0;
-  const int nwords = (nb + 63) / 64;
-  for (int w0 = 0; w0 < nwords; w0 += 64) {
-    const int wi = w0 + lane;
-    const uint64_t word = wi < nwords ? sh.sel[wi] : 0ull;
-    const int c = __popcll(word);
-    int incl = c;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += y;
-    }
-    int p = pos + incl - c;
-    uint64_t m = word;
-    while (m) {
-      const int bit = __builtin_ctzll(m);
-      m &= m - 1;
-      if (p < k) out[p] = 64 * wi + bit;
-      ++p;
-    }
-    pos += __shfl(incl, 63, 64);
-  }
-  for (int t = pos + lane; t < k; t += 64) out[t] = -1;
+  const int nsel = min(sh.cnt[3], 64);
+  const uint32_t y = lane < nsel ? ~(uint32_t)sh.sel[lane] : 0u;  // descending ~id = ascending id
+  const uint32_t srt = bitonic32_sizes<2>(y);
+  if (lane < k) out[lane] = lane < nsel ? (int)~srt : -1;
 }
 
 size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks) {
@@ -842,10 +830,17 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.format == 1)
-    hipLaunchKernelGGL(index_select_kernel<1>, dim3((unsigned)a.num_rows), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(index_select_kernel<2>, dim3((unsigned)a.num_rows), dim3(256), 0, stream, a);
+  const dim3 g((unsigned)a.num_rows), blk(256);
+  if (a.max_blocks <= 256 * 8) {
+    if (a.format == 1) hipLaunchKernelGGL((index_select_kernel<1, 8>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((index_select_kernel<2, 8>), g, blk, 0, stream, a);
+  } else if (a.max_blocks <= 256 * 16) {
+    if (a.format == 1) hipLaunchKernelGGL((index_select_kernel<1, 16>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((index_select_kernel<2, 16>), g, blk, 0, stream, a);
+  } else {
+    if (a.format == 1) hipLaunchKernelGGL((index_select_kernel<1, 32>), g, blk, 0, stream, a);
+    else hipLaunchKernelGGL((index_select_kernel<2, 32>), g, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
