@@ -35,6 +35,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "fp4.hpp"
 #include "launch.hpp"
 
@@ -452,7 +454,7 @@ struct SelectShared {
   int band[kBandCap];
   int bpage[kBandCap];
   double dots[kBandCap];
-  double q[kDim];
+  alignas(16) double q[kDim];
   uint32_t thr[4];
   float red[4];
   int ired[4];
@@ -717,7 +719,13 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
           double acc = 0.0, mag = 0.0;
           int lk = INT_MAX;
           if (pg[u] >= 0) {
-            double svd[SB / 2];
+            // NVFP4: k = code * scale is exact in fp32 (at most 6 significant bits,
+            // within [2^-10, 2688]); MXFP4 scales span 2^-127 .. 2^127, so k is
+            // formed in float64. Every product and partial sum is exact in float64
+            // under the check below, so the eight independent chains (they change
+            // latency, not the result) give the exact sum.
+            typedef typename std::conditional<FMT == 1, float, double>::type kscale_t;
+            kscale_t sf[SB / 2];
 #pragma unroll
             for (int g = 0; g < SB / 2; ++g) {
               const uint32_t byte = (sb4[u] >> (8 * g)) & 0xFFu;
@@ -726,14 +734,16 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
                 const uint32_t e = (byte >> 3) & 15u, mm = byte & 7u;
                 const uint32_t M = e ? (mm | 8u) : mm;
                 const int ex = e ? (int)e - 10 : -9;
-                svd[g] = __builtin_ldexp((double)M, ex);
+                sf[g] = (kscale_t)__builtin_ldexpf((float)M, ex);
                 lsb = M ? ex + __builtin_ctz(M) : INT_MAX;
               } else {
-                svd[g] = __builtin_ldexp(1.0, (int)byte - 127);
+                sf[g] = (kscale_t)__builtin_ldexp(1.0, (int)byte - 127);
                 lsb = (int)byte - 127;
               }
               if (lsb != INT_MAX) lk = min(lk, lsb - 1);  // codes are multiples of 1/2
             }
+            double av[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+            double mv[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
 #pragma unroll
             for (int wi = 0; wi < 8; ++wi) {
               const uint32_t word = wi < 4 ? w0[u][wi] : w1[u][wi - 4];
@@ -747,15 +757,17 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
                   default: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); pr = make_float2(x[0], x[1]); break; }
                 }
                 const int dd = 8 * wi + 2 * bs;
-                const double s_ = svd[FMT == 1 ? (dd >> 4) : (dd >> 5)];
-                const double k0 = (double)pr.x * s_, k1 = (double)pr.y * s_;
-                const double q0 = sh.q[64 * h + dd], q1 = sh.q[64 * h + dd + 1];
-                acc = __builtin_fma(q0, k0, acc);
-                acc = __builtin_fma(q1, k1, acc);
-                mag = __builtin_fma(fabs(q0), fabs(k0), mag);
-                mag = __builtin_fma(fabs(q1), fabs(k1), mag);
+                const kscale_t s_ = sf[FMT == 1 ? (dd >> 4) : (dd >> 5)];
+                const double k0 = (double)((kscale_t)pr.x * s_), k1 = (double)((kscale_t)pr.y * s_);
+                const double2 qq = *reinterpret_cast<const double2*>(&sh.q[64 * h + dd]);
+                av[2 * bs] = __builtin_fma(qq.x, k0, av[2 * bs]);
+                av[2 * bs + 1] = __builtin_fma(qq.y, k1, av[2 * bs + 1]);
+                mv[2 * bs] = __builtin_fma(fabs(qq.x), fabs(k0), mv[2 * bs]);
+                mv[2 * bs + 1] = __builtin_fma(fabs(qq.y), fabs(k1), mv[2 * bs + 1]);
               }
             }
+            acc = ((av[0] + av[1]) + (av[2] + av[3])) + ((av[4] + av[5]) + (av[6] + av[7]));
+            mag = ((mv[0] + mv[1]) + (mv[2] + mv[3])) + ((mv[4] + mv[5]) + (mv[6] + mv[7]));
           }
           acc += lane_xor<1>(acc);  // the two halves of a token sit in lanes 2u, 2u + 1
           mag += lane_xor<1>(mag);
