@@ -109,10 +109,10 @@ struct QueryTile {
 // qe0 = sum of |r|: the scorer's error bound is 6 smax (2^-15 qs0 + qe0) per
 // block, the 2^-15 covering any order of the <= 383 fp32 additions of the three
 // chained MFMAs (383 * 2^-24 < 2^-15).
-__device__ __forceinline__ void load_query_mx(QueryTile& q, const IndexArgs& a, int n, int G) {
+__device__ __forceinline__ void build_query_mx(QueryTile& q, const IndexArgs& a, int row, int n, int G) {
   u32x4 raw[4] = {};
-  if (n < q.ql) {
-    const uint16_t* qp = a.q_idx + (int64_t)(q.r0 + n) * a.q_stride;
+  if (row >= 0) {
+    const uint16_t* qp = a.q_idx + (int64_t)row * a.q_stride;
     raw[0] = *reinterpret_cast<const u32x4*>(qp + 16 * G);
     raw[1] = *reinterpret_cast<const u32x4*>(qp + 16 * G + 8);
     raw[2] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G);
@@ -194,20 +194,17 @@ __device__ __forceinline__ void load_query_mx(QueryTile& q, const IndexArgs& a, 
   q.unscale = 1.0f;
 }
 
+// The B operand of query row `row` (or zeros when row < 0) in lane (n, G), with
+// the sums the error bound needs. Lanes n of one 16-lane column share a row.
 template <int FMT>
-__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int n, int G) {
-  q.b = b;
-  q.r0 = a.cu_q[b];
-  q.ql = a.cu_q[b + 1] - q.r0;
-  q.min_len = a.row_len[q.r0];
-  q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
+__device__ __forceinline__ void build_query(QueryTile& q, const IndexArgs& a, int row, int n, int G) {
   if (FMT == 2) {
-    load_query_mx(q, a, n, G);
+    build_query_mx(q, a, row, n, G);
     return;
   }
   u32x4 raw[4] = {};
-  if (n < q.ql) {
-    const uint16_t* qp = a.q_idx + (int64_t)(q.r0 + n) * a.q_stride + 32 * G;
+  if (row >= 0) {
+    const uint16_t* qp = a.q_idx + (int64_t)row * a.q_stride + 32 * G;
 #pragma unroll
     for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
@@ -236,6 +233,41 @@ __device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int
   }
 }
 
+template <int FMT>
+__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int n, int G) {
+  q.b = b;
+  q.r0 = a.cu_q[b];
+  q.ql = a.cu_q[b + 1] - q.r0;
+  q.min_len = a.row_len[q.r0];
+  q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
+  build_query<FMT>(q, a, n < q.ql ? q.r0 + n : -1, n, G);
+}
+
+// S^T tile i of a page: acc[v] = (scaled) score of token 16 i + 4 G + v against
+// the query in column n (lane (n, G)); NVFP4 also returns the tile's scales.
+template <int FMT>
+__device__ __forceinline__ f32x4 tile_scores(const PageBuf& p, const QueryTile& q, int i, f16x2& sc) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (FMT == 1) {
+    // both E4M3 scales of the lane's two groups in one conversion (OCP E4M3FN, exact)
+    const auto sf = __builtin_amdgcn_cvt_pk_f32_fp8((int)p.ks[i], false);
+    sc = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[1]));
+    const f16x8 s0 = {sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+    const f16x8 s1 = {sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+    acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][0]) * s0, q.op[0], acc);
+    acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][1]) * s0, q.op[1], acc);
+    acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][2]) * s1, q.op[2], acc);
+    acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][3]) * s1, q.op[3], acc);
+  } else {
+    // the lane's 32 codes and E8M0 byte are the fp4 A operand and its scale as loaded
+    const i32x8 ka = {(int)p.kr[i][0], (int)p.kr[i][1], (int)p.kr[i][2], (int)p.kr[i][3], 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q.qb[t], acc, 4, 0, 0, (int)p.ks[i], 0, q.qsc[t]);
+  }
+  return acc;
+}
+
 // Score one page against the request's rows; write the fp32 score and error bound.
 template <int FMT>
 __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q, const IndexArgs& a, int j, int n,
@@ -246,26 +278,10 @@ __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q,
   float smx_mx = 0.f;                          // MXFP4: largest E8M0 scale of group G
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (FMT == 1) {
-      // both E4M3 scales of the lane's two groups in one conversion (OCP E4M3FN, exact)
-      const auto sf = __builtin_amdgcn_cvt_pk_f32_fp8((int)p.ks[i], false);
-      const f16x2 sc = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[1]));
-      smx = __builtin_elementwise_max(smx, sc);
-      const f16x8 s0 = {sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
-      const f16x8 s1 = {sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
-      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][0]) * s0, q.op[0], acc);
-      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][1]) * s0, q.op[1], acc);
-      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][2]) * s1, q.op[2], acc);
-      acc = mfma_f16(fp4x8_to_f16_unscaled(p.kr[i][3]) * s1, q.op[3], acc);
-    } else {
-      // the lane's 32 codes and E8M0 byte are the fp4 A operand and its scale as loaded
-      smx_mx = fmaxf(smx_mx, e8m0_to_f32(p.ks[i]));
-      const i32x8 ka = {(int)p.kr[i][0], (int)p.kr[i][1], (int)p.kr[i][2], (int)p.kr[i][3], 0, 0, 0, 0};
-#pragma unroll
-      for (int t = 0; t < 3; ++t)
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q.qb[t], acc, 4, 0, 0, (int)p.ks[i], 0, q.qsc[t]);
-    }
+    f16x2 sc;
+    f32x4 acc = tile_scores<FMT>(p, q, i, sc);
+    if (FMT == 1) smx = __builtin_elementwise_max(smx, sc);
+    else smx_mx = fmaxf(smx_mx, e8m0_to_f32(p.ks[i]));
     if (need_mask) {
       const int t0 = j * kPage + 16 * i + 4 * G;
 #pragma unroll
@@ -453,6 +469,7 @@ struct SelectShared {
   uint64_t cand[64];
   int band[kBandCap];
   int bpage[kBandCap];
+  float bdel[kBandCap];
   double dots[kBandCap];
   alignas(16) double q[kDim];
   uint32_t thr[4];
@@ -462,18 +479,6 @@ struct SelectShared {
   uint64_t keys[2];
   int sel[64];
 };
-
-__device__ __forceinline__ void lds_max_f64(double* p, double v) {
-  unsigned long long* u = reinterpret_cast<unsigned long long*>(p);
-  unsigned long long cur = *u;
-  while (true) {
-    const double c = __longlong_as_double((long long)cur);
-    if (!(v > c)) break;
-    const unsigned long long prev = atomicCAS(u, cur, (unsigned long long)__double_as_longlong(v));
-    if (prev == cur) break;
-    cur = prev;
-  }
-}
 
 // bitonic network over one u32 per lane, descending across the wave
 template <int SIZE, int STRIDE>
@@ -669,7 +674,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
         if (slot < kBandCap) {
           sh.band[slot] = j;
           sh.bpage[slot] = pv[i];
-          sh.dots[slot] = -INFINITY;
+          sh.bdel[slot] = bv[i];
         }
       }
     }
@@ -685,100 +690,89 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       mode = 0;
     } else {
       mode = 2;
-      // exact rescore: thread (t, h) takes token t, dims [64 h, 64 h + 64) of up
-      // to four band blocks per batch, loading all four before computing
+      // exact rescore, one band block per wave. The wave first re-scores the
+      // block's tokens with the scan's own arithmetic (same query operand, same
+      // MFMA), so the bound the scan stored for this row and block bounds every
+      // token's error d: only tokens within 2 d of the block's approximate
+      // maximum can hold the exact maximum. Each of those is then summed exactly
+      // in float64 by the whole wave (lane l: dims 2l, 2l+1), its data taken from
+      // the wave's page registers.
       bool inexact = false;
-      constexpr int kBatch = 4;
-      const int t = tid >> 1, h = tid & 1;
-#pragma unroll 1
-      for (int m0 = 0; m0 < nband; m0 += kBatch) {
-        u32x4 w0[kBatch], w1[kBatch];
-        uint32_t sb4[kBatch];
-        int pg[kBatch];
+      const int n = lane & 15, G = lane >> 4;
+      QueryTile qt;
+      build_query<FMT>(qt, a, n == 0 ? r : -1, n, G);  // column 0: this row
+      const double2 qq = *reinterpret_cast<const double2*>(&sh.q[2 * lane]);
+      for (int m = w; m < nband; m += 4) {
+        const int j = sh.band[m];
+        const int page = sh.bpage[m];
+        double best = -INFINITY;
+        if (page >= 0 && page < a.num_pages) {
+          PageBuf pb;
+          load_page<FMT>(pb, a, page, n, G);
+          const int t_lim = len - j * kPage;  // causal tokens of the block
+          f32x4 ts[8];
+          float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int m = m0 + u;
-          pg[u] = -1;
-          if (m < nband) {
-            const int page = sh.bpage[m];
-            if (page >= 0 && page < a.num_pages) {
-              pg[u] = page;
-              const uint8_t* pp = a.idx_data + (int64_t)page * (kPage * kPayload) + t * kPayload + 32 * h;
-              w0[u] = *reinterpret_cast<const u32x4*>(pp);
-              w1[u] = *reinterpret_cast<const u32x4*>(pp + 16);
-              const uint8_t* spp = a.idx_scale + (int64_t)page * (kPage * SB) + t * SB + (SB / 2) * h;
-              sb4[u] = FMT == 1 ? *reinterpret_cast<const uint32_t*>(spp) : (uint32_t)*reinterpret_cast<const uint16_t*>(spp);
+          for (int i = 0; i < 8; ++i) {
+            f16x2 unused;
+            ts[i] = tile_scores<FMT>(pb, qt, i, unused) * qt.unscale;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              if (n != 0 || 16 * i + 4 * G + v >= t_lim) ts[i][v] = -INFINITY;
+              mx = fmaxf(mx, ts[i][v]);
             }
           }
-        }
-#pragma unroll 1
-        for (int u = 0; u < kBatch; ++u) {
-          const int m = m0 + u;
-          if (m >= nband) break;
-          const int j = sh.band[m];
-          double acc = 0.0, mag = 0.0;
-          int lk = INT_MAX;
-          if (pg[u] >= 0) {
-            // NVFP4: k = code * scale is exact in fp32 (at most 6 significant bits,
-            // within [2^-10, 2688]); MXFP4 scales span 2^-127 .. 2^127, so k is
-            // formed in float64. Every product and partial sum is exact in float64
-            // under the check below, so the eight independent chains (they change
-            // latency, not the result) give the exact sum.
-            typedef typename std::conditional<FMT == 1, float, double>::type kscale_t;
-            kscale_t sf[SB / 2];
+          mx = lane_fmax<1, 64>(mx);
+          const double thr = (double)mx - 2.0 * (double)sh.bdel[m];
 #pragma unroll
-            for (int g = 0; g < SB / 2; ++g) {
-              const uint32_t byte = (sb4[u] >> (8 * g)) & 0xFFu;
-              int lsb;
-              if (FMT == 1) {
-                const uint32_t e = (byte >> 3) & 15u, mm = byte & 7u;
-                const uint32_t M = e ? (mm | 8u) : mm;
-                const int ex = e ? (int)e - 10 : -9;
-                sf[g] = (kscale_t)__builtin_ldexpf((float)M, ex);
-                lsb = M ? ex + __builtin_ctz(M) : INT_MAX;
-              } else {
-                sf[g] = (kscale_t)__builtin_ldexp(1.0, (int)byte - 127);
-                lsb = (int)byte - 127;
-              }
-              if (lsb != INT_MAX) lk = min(lk, lsb - 1);  // codes are multiples of 1/2
-            }
-            double av[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-            double mv[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+          for (int i = 0; i < 8; ++i) {
+            uint32_t cm = 0;
 #pragma unroll
-            for (int wi = 0; wi < 8; ++wi) {
-              const uint32_t word = wi < 4 ? w0[u][wi] : w1[u][wi - 4];
-#pragma unroll
-              for (int bs = 0; bs < 4; ++bs) {
-                float2 pr;
-                switch (bs) {
-                  case 0: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); pr = make_float2(x[0], x[1]); break; }
-                  case 1: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); pr = make_float2(x[0], x[1]); break; }
-                  case 2: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); pr = make_float2(x[0], x[1]); break; }
-                  default: { auto x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); pr = make_float2(x[0], x[1]); break; }
+            for (int v = 0; v < 4; ++v) cm |= ((double)ts[i][v] >= thr ? 1u : 0u) << v;
+            uint64_t holders = __ballot(cm != 0);
+            while (holders) {
+              const int src = __builtin_ctzll(holders);
+              holders &= holders - 1;
+              uint32_t bits = __shfl(cm, src, 64);
+              while (bits) {
+                const int v = __builtin_ctz(bits);
+                bits &= bits - 1;
+                const int nt = 4 * (src >> 4) + v;  // token 16 i + nt of the block
+                const int s2 = nt + 16 * G;         // lane holding dims [32 G, 32 G + 32) of it
+                const uint32_t w0 = __shfl(pb.kr[i][0], s2, 64), w1 = __shfl(pb.kr[i][1], s2, 64);
+                const uint32_t w2 = __shfl(pb.kr[i][2], s2, 64), w3 = __shfl(pb.kr[i][3], s2, 64);
+                const uint32_t sk = __shfl(pb.ks[i], s2, 64);
+                const int ww = (lane & 15) >> 2;
+                const uint32_t word = ww == 0 ? w0 : (ww == 1 ? w1 : (ww == 2 ? w2 : w3));
+                const uint32_t byte = (word >> (8 * (lane & 3))) & 0xFFu;
+                const auto cd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+                double sd;
+                int lsb;
+                if (FMT == 1) {
+                  const uint32_t sb = (sk >> (8 * ((lane & 15) >> 3))) & 0xFFu;
+                  const uint32_t e = (sb >> 3) & 15u, mm = sb & 7u;
+                  const uint32_t M = e ? (mm | 8u) : mm;
+                  const int ex = e ? (int)e - 10 : -9;
+                  sd = __builtin_ldexp((double)M, ex);
+                  lsb = M ? ex + __builtin_ctz(M) - 1 : INT_MAX;  // codes are multiples of 1/2
+                } else {
+                  sd = __builtin_ldexp(1.0, (int)(sk & 0xFFu) - 127);
+                  lsb = (int)(sk & 0xFFu) - 128;
                 }
-                const int dd = 8 * wi + 2 * bs;
-                const kscale_t s_ = sf[FMT == 1 ? (dd >> 4) : (dd >> 5)];
-                const double k0 = (double)((kscale_t)pr.x * s_), k1 = (double)((kscale_t)pr.y * s_);
-                const double2 qq = *reinterpret_cast<const double2*>(&sh.q[64 * h + dd]);
-                av[2 * bs] = __builtin_fma(qq.x, k0, av[2 * bs]);
-                av[2 * bs + 1] = __builtin_fma(qq.y, k1, av[2 * bs + 1]);
-                mv[2 * bs] = __builtin_fma(fabs(qq.x), fabs(k0), mv[2 * bs]);
-                mv[2 * bs + 1] = __builtin_fma(fabs(qq.y), fabs(k1), mv[2 * bs + 1]);
+                const double k0 = (double)cd[0] * sd, k1 = (double)cd[1] * sd;
+                double dot = __builtin_fma(qq.x, k0, qq.y * k1);
+                double mag = __builtin_fma(fabs(qq.x), fabs(k0), fabs(qq.y * k1));
+                dot = lane_reduce<1, 64>(dot, [](double x, double y) { return x + y; });
+                mag = lane_reduce<1, 64>(mag, [](double x, double y) { return x + y; });
+                const int lk = lane_reduce<1, 64>(lsb, [](int x, int y) { return x < y ? x : y; });
+                if (mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
+                  inexact = true;
+                best = fmax(best, dot + 0.0);
               }
             }
-            acc = ((av[0] + av[1]) + (av[2] + av[3])) + ((av[4] + av[5]) + (av[6] + av[7]));
-            mag = ((mv[0] + mv[1]) + (mv[2] + mv[3])) + ((mv[4] + mv[5]) + (mv[6] + mv[7]));
           }
-          acc += lane_xor<1>(acc);  // the two halves of a token sit in lanes 2u, 2u + 1
-          mag += lane_xor<1>(mag);
-          lk = min(lk, lane_xor<1>(lk));
-          const bool valid = pg[u] >= 0 && (j * kPage + t < len);
-          if (valid && mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
-            inexact = true;
-          double v = valid ? acc + 0.0 : -INFINITY;
-          v = lane_reduce<1, 64>(v, [](double x, double y) { return fmax(x, y); });
-          if (lane == 0) lds_max_f64(&sh.dots[m], v);
         }
+        if (lane == 0) sh.dots[m] = best;
       }
       if (inexact) set_status(a.status, kDevInexact);
       __syncthreads();
