@@ -43,7 +43,7 @@ m3s_status check_table(const int32_t* bt, int32_t bt_stride, int32_t max_blocks)
 }
 
 int scan_grid() {
-  // one 8-wave scan workgroup per CU of the current device
+  // one 16-wave scan workgroup per CU of the current device
   static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;

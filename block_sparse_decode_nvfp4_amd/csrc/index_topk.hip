@@ -309,13 +309,14 @@ __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q,
 }
 
 // Streaming scan. The (request, block) units of all requests form one flat list
-// (block fastest). Workgroup g (8 waves, one per CU) takes the contiguous slice
+// (block fastest). Workgroup g (16 waves, one per CU) takes the contiguous slice
 // [g * N / W, (g + 1) * N / W), so consecutive slices of a long request land on
 // different XCDs. The slice's block-table entries are staged in LDS, and its
 // waves claim units one at a time from an LDS counter: a wave whose pages arrive
 // late simply takes fewer units, so the waves of a workgroup finish together.
-// Each wave keeps two pages in flight (one scoring, one loading).
-constexpr int kScanWaves = 8;
+// Each wave keeps one page in flight: measured, 16 waves with one page each beat
+// 8 waves with two or three (deeper per-wave prefetch only deepens the queue).
+constexpr int kScanWaves = 16;
 constexpr int kScanChunk = 1024;  // units staged in LDS at a time
 
 template <int FMT>
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a
 
   QueryTile qt;
   qt.b = -1;
-  PageBuf pa, pb;
+  PageBuf pa;
   auto process = [&](const PageBuf& buf, int i) {
     const int key = s_unit[i];
     if (key < 0) return;
@@ -386,21 +387,12 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a
     }
     if (tid == 0) s_ctr = 0;
     __syncthreads();
-    // claims of a wave increase, so the units are scored in claim order and the
-    // first claim past the chunk ends the wave's work on it
-    int i0 = claim();
-    if (i0 < cnt && s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
-    int i1 = claim();
-    if (i1 < cnt && s_page[i1] >= 0) load_page<FMT>(pb, a, s_page[i1], n, G);
+    // one page in flight per wave; the other waves of the SIMD cover its latency
     while (true) {
+      const int i0 = claim();
       if (i0 >= cnt) break;
+      if (s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
       process(pa, i0);
-      i0 = claim();
-      if (i0 < cnt && s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
-      if (i1 >= cnt) break;
-      process(pb, i1);
-      i1 = claim();
-      if (i1 < cnt && s_page[i1] >= 0) load_page<FMT>(pb, a, s_page[i1], n, G);
     }
     __syncthreads();  // the chunk's LDS tables are rewritten next
   }
