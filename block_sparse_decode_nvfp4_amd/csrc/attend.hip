@@ -293,29 +293,49 @@ __global__ __launch_bounds__(kWaves * 64) void attend_split_kernel(AttendArgs a)
   }
 }
 
+// All partials of the row are loaded before any is used (one round trip);
+// nsplit <= kMaxSplits.
+constexpr int kMaxSplits = (64 + kBlocks - 1) / kBlocks;
+
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int hh = tid >> 4, d0 = (tid & 15) * 8;
   if (hh >= a.num_heads) return;
-  float M = -INFINITY;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[(((int64_t)r * a.nsplit + s) * 16 + hh) * 2]);
-  float L = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float* ml = a.part_ml + (((int64_t)r * a.nsplit + s) * 16 + hh) * 2;
-      const float f = __builtin_amdgcn_exp2f(ml[0] - M);
-      L += f * ml[1];
-      const float* po = a.part_o + (((int64_t)r * a.nsplit + s) * 16 + hh) * kDim + d0;
+  float mv[kMaxSplits], lv[kMaxSplits];
+  f32x4 ov[kMaxSplits][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += f * po[e];
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < a.nsplit) {
+      const float* ml = a.part_ml + (((int64_t)r * a.nsplit + s) * 16 + hh) * 2;
+      const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + (((int64_t)r * a.nsplit + s) * 16 + hh) * kDim + d0);
+      mv[s] = ml[0];
+      lv[s] = ml[1];
+      ov[s][0] = po[0];
+      ov[s][1] = po[1];
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < a.nsplit) M = fmaxf(M, mv[s]);
+  float L = 0.f;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < a.nsplit) {
+        const float f = __builtin_amdgcn_exp2f(mv[s] - M);
+        L += f * lv[s];
+        acc0 += f * ov[s][0];
+        acc1 += f * ov[s][1];
+      }
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  float* dst = a.out + ((int64_t)r * a.num_heads + hh) * kDim + d0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) dst[e] = acc[e] * inv;
+  f32x4* dst = reinterpret_cast<f32x4*>(a.out + ((int64_t)r * a.num_heads + hh) * kDim + d0);
+  dst[0] = acc0 * inv;
+  dst[1] = acc1 * inv;
 }
 
 int32_t attend_nsplit(int32_t topk) { return (topk + kBlocks - 1) / kBlocks; }

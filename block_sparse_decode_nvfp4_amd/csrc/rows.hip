@@ -16,15 +16,13 @@ constexpr int kRowsThreads = 1024;
 
 __global__ __launch_bounds__(kRowsThreads) void decode_rows_kernel(RowsArgs a) {
   __shared__ int s_scan[kRowsThreads / 64];
-  __shared__ int s_carry;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wid = tid >> 6;
-  if (tid == 0) s_carry = 0;
   const int B = a.num_reqs;
+  // every load of the launch is independent of the others: issued at once
   const int q_first = a.cu_q[0];
   const int q_end = a.cu_q[B];
-  if (tid == 0 && (q_first != 0 || q_end > a.num_rows || q_end < 0)) set_status(a.status, kDevBadRows);
-  __syncthreads();
+  int carry = 0;  // blocks of the requests before this chunk (uniform)
   for (int base = 0; base < B; base += kRowsThreads) {
     const int b = base + tid;
     int nblk = 0;
@@ -68,13 +66,14 @@ __global__ __launch_bounds__(kRowsThreads) void decode_rows_kernel(RowsArgs a) {
     }
     __syncthreads();
     const int wave_base = wid ? s_scan[wid - 1] : 0;
-    const int carry = s_carry;
     if (b < B) a.req_blk[b] = carry + wave_base + x - nblk;
-    __syncthreads();
-    if (tid == kRowsThreads - 1) s_carry = carry + s_scan[kRowsThreads / 64 - 1];
-    __syncthreads();
+    carry += s_scan[kRowsThreads / 64 - 1];
+    __syncthreads();  // s_scan is rewritten by the next chunk
   }
-  if (tid == 0) a.req_blk[B] = s_carry;
+  if (tid == 0) {
+    a.req_blk[B] = carry;
+    if (q_first != 0 || q_end > a.num_rows || q_end < 0) set_status(a.status, kDevBadRows);
+  }
   // pad rows after the last request, and before cu_q[0] if it is not 0
   const int lo = q_end < 0 ? 0 : (q_end > a.num_rows ? a.num_rows : q_end);
   for (int r = lo + tid; r < a.num_rows; r += kRowsThreads) {
