@@ -16,7 +16,9 @@ Each function follows the pages:
   * topk_blocks: the k best blocks; equal scores go to the lower block id by
     default (or to the higher id, the rule of the ATOM review notes on
     ``_pack_score_key``); ids are emitted ascending, padded with -1 (the fused
-    top-k "emits ascending ids").
+    top-k "emits ascending ids"). Forced initial / local blocks (vLLM PR
+    "MXFP4 KV + indexer cache for MiniMax-M3.1", Design; ATOM review notes on
+    init_blocks + local_blocks > topk) rank above every scored block.
   * attend_row: softmax attention of the row's G query heads over the tokens
     of the selected blocks that are causal for the row, with the dequantized
     K/V (ATOM PR "NVFP4 sparse KV", Tests: "against the dequantized
@@ -126,11 +128,39 @@ def block_scores(q: np.ndarray, khat: np.ndarray, row_len: int) -> np.ndarray:
     return s + 0.0          # -0.0 -> +0.0: equal scores compare equal
 
 
-def topk_blocks(scores: np.ndarray, k: int, tie_high: bool = False) -> np.ndarray:
-    """The k best blocks by (score descending, id ascending | descending), emitted ascending, -1 padded."""
+def forced_class(nb: int, init_blocks: int = 0, local_blocks: int = 0) -> np.ndarray:
+    """Per causal block: 2 for a forced initial block (id < init_blocks), 1 for a forced
+    local block (one of the row's newest local_blocks blocks), else 0.
+
+    Reading of the vLLM PR "MXFP4 KV + indexer cache for MiniMax-M3.1" (Design: the
+    init / local sentinels 1e30 / 1e29 written on a row's causal blocks before its
+    top-k) and of the ATOM review notes on init_blocks + local_blocks > topk: an
+    initial block outranks a local one (its sentinel is the larger), both outrank every
+    scored block, and a block that is both counts as initial.
+    """
+    j = np.arange(nb)
+    cls = np.zeros(nb, dtype=np.int64)
+    cls[j >= nb - local_blocks] = 1
+    cls[j < init_blocks] = 2
+    return cls
+
+
+def topk_blocks(scores: np.ndarray, k: int, tie_high: bool = False, init_blocks: int = 0,
+                local_blocks: int = 0) -> np.ndarray:
+    """The k best blocks, emitted ascending, -1 padded.
+
+    Order: forced class descending (``forced_class``); inside a forced class the higher
+    id first (the ATOM review: with init + local > topk the newest local blocks, the
+    row's own block among them, must be kept); among scored blocks score descending,
+    then id ascending (descending with ``tie_high``).
+    """
     nb = len(scores)
     ids = np.arange(nb)
-    order = np.lexsort((-ids if tie_high else ids, -np.asarray(scores, dtype=np.float64)))
+    cls = forced_class(nb, init_blocks, local_blocks)
+    s = np.asarray(scores, dtype=np.float64)
+    tie = np.where(cls > 0, -ids, -ids if tie_high else ids)
+    score_key = np.where(cls > 0, 0.0, -s)
+    order = np.lexsort((tie, score_key, -cls))
     sel = np.sort(order[: min(k, nb)])
     out = np.full(k, -1, dtype=np.int32)
     out[: len(sel)] = sel
@@ -174,7 +204,7 @@ def request_rows(cu_q, b):
 
 
 def step(planes, fmt, new_rows, new_slots, cu_q, seq_lens, block_table, q_idx_bits, q_bits,
-         topk, sm_scale, num_rows=None, tie_high=False, requests=None):
+         topk, sm_scale, num_rows=None, tie_high=False, requests=None, init_blocks=0, local_blocks=0):
     """One decode step: store -> decode_rows -> per row scores, top-k, attention.
 
     ``requests`` restricts the score / top-k / attention work to a subset of
@@ -196,7 +226,8 @@ def step(planes, fmt, new_rows, new_slots, cu_q, seq_lens, block_table, q_idx_bi
         rows = list(request_rows(cu_q, b))
         sel = {}
         for r in rows:
-            ids[r] = topk_blocks(block_scores(qi[r], kidx, int(row_len[r])), topk, tie_high)
+            ids[r] = topk_blocks(block_scores(qi[r], kidx, int(row_len[r])), topk, tie_high, init_blocks,
+                                 local_blocks)
             sel[r] = ids[r]
         need = sorted({int(j) for r in rows for j in sel[r] if j >= 0})
         kh = np.zeros((n, F.HEAD_DIM))

@@ -288,3 +288,55 @@ def test_step_matches_brute_force_tiny():
         p = np.exp(lg - lg.max(1, keepdims=True))
         ref = (p / p.sum(1, keepdims=True)) @ vh[t]
         assert np.allclose(out[r], ref, rtol=1e-12, atol=1e-14)
+
+
+# ---- forced initial / local blocks (vLLM PR "MXFP4 KV + indexer cache for MiniMax-M3.1",
+# Design; ATOM PR "[MiniMax-M3.1] FP4 index cache and NVFP4 sparse KV cache", review
+# notes on init_blocks + local_blocks > topk). Expected selections worked by hand.
+
+def test_forced_review_example_keeps_newest_local_blocks():
+    """topk 16, init 4, local 16 on a long row: the review's failing kernel picked 0-3 and
+    n-16..n-5; the kept set must be the 4 initial blocks and the 12 newest local ones,
+    the row's own block n-1 among them."""
+    n = 100
+    scores = np.arange(n, dtype=np.float64)[::-1].copy()  # real scores favour low ids
+    got = P.topk_blocks(scores, 16, init_blocks=4, local_blocks=16).tolist()
+    assert got == [0, 1, 2, 3] + list(range(88, 100))
+    assert n - 1 in got
+
+
+def test_forced_blocks_fit_then_best_scores_fill():
+    """init 2 + local 3 <= k 8 on 20 blocks with score = id: forced {0, 1, 17, 18, 19},
+    then the best scored blocks 16, 15, 14."""
+    scores = np.arange(20, dtype=np.float64)
+    assert P.topk_blocks(scores, 8, init_blocks=2, local_blocks=3).tolist() == [0, 1, 14, 15, 16, 17, 18, 19]
+
+
+def test_forced_overlap_counts_as_initial():
+    """5 blocks, init 4, local 3, k 4: blocks 2, 3 are both; as initial blocks they rank
+    with 0, 1 above the local block 4."""
+    scores = np.array([0.0, 0.0, 0.0, 0.0, 9.0])
+    assert P.topk_blocks(scores, 4, init_blocks=4, local_blocks=3).tolist() == [0, 1, 2, 3]
+    assert P.forced_class(5, 4, 3).tolist() == [2, 2, 2, 2, 1]
+
+
+def test_forced_ties_go_to_higher_ids_even_with_low_id_rule():
+    """init 10 > k 4: the 4 highest initial ids are kept, whatever the scored tie rule."""
+    scores = np.zeros(30)
+    for tie_high in (False, True):
+        assert P.topk_blocks(scores, 4, tie_high, init_blocks=10).tolist() == [6, 7, 8, 9]
+    assert P.topk_blocks(scores, 4, local_blocks=10).tolist() == [26, 27, 28, 29]
+
+
+def test_forced_blocks_outrank_any_score():
+    scores = np.full(12, -1.0)
+    scores[5] = 1e300
+    assert P.topk_blocks(scores, 3, init_blocks=1, local_blocks=1).tolist() == [0, 5, 11]
+    assert P.topk_blocks(scores, 2, init_blocks=1, local_blocks=1).tolist() == [0, 11]
+
+
+def test_forced_zero_is_plain_topk_and_short_rows_take_all():
+    rng = np.random.default_rng(3)
+    s = rng.standard_normal(50)
+    assert P.topk_blocks(s, 7).tolist() == P.topk_blocks(s, 7, init_blocks=0, local_blocks=0).tolist()
+    assert P.topk_blocks(s[:5], 8, init_blocks=3, local_blocks=3).tolist() == [0, 1, 2, 3, 4, -1, -1, -1]
