@@ -72,7 +72,7 @@ def load(path: str | None = None):
     sig = {
         "m3s_store": (I32, [V, V, V, V, I64, V, I32, V, V]),
         "m3s_decode_rows": (I32, [V, V, I32, I32, V, V, V, V, V]),
-        "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, V, V, SZ, V, V]),
+        "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, I32, I32, V, V, SZ, V, V]),
         "m3s_sparse_attend": (I32, [V, V, I64, I64, I32, V, I32, I32, V, V, I32, F32, V, V, SZ, V, V]),
         "m3s_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "m3s_read_device_status": (I32, [V, V, V]),
@@ -218,7 +218,8 @@ def attend_workspace(rows: Rows, max_blocks: int, topk: int, num_heads: int, dev
 
 
 def m3s_index_topk(cache: Cache, q_idx, block_table, max_blocks: int, rows: Rows, topk: int, flags: int = 0,
-                   topk_ids=None, workspace=None, dev_status=None, stream=None):
+                   topk_ids=None, workspace=None, dev_status=None, stream=None, init_blocks: int = 0,
+                   local_blocks: int = 0):
     torch = _torch()
     _need(q_idx, "q_idx", torch.bfloat16)
     _need(block_table, "block_table", torch.int32)
@@ -231,8 +232,8 @@ def m3s_index_topk(cache: Cache, q_idx, block_table, max_blocks: int, rows: Rows
     if workspace is None:
         workspace = index_workspace(rows, max_blocks, topk, q_idx.device)
     st = load().m3s_index_topk(cache.ref(), _ptr(q_idx), q_idx.stride(0), _ptr(block_table), block_table.stride(0),
-                               max_blocks, rows.ref(), topk, flags, _ptr(topk_ids), _ptr(workspace),
-                               workspace.numel(), _ptr(dev_status), _stream(stream))
+                               max_blocks, rows.ref(), topk, flags, init_blocks, local_blocks, _ptr(topk_ids),
+                               _ptr(workspace), workspace.numel(), _ptr(dev_status), _stream(stream))
     _check("m3s_index_topk", st)
     return topk_ids
 

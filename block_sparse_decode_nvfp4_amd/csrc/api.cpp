@@ -144,7 +144,8 @@ m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t
 
 m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
                           const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, const m3s_rows* rows,
-                          int32_t topk, int32_t flags, int32_t* topk_ids, void* workspace, size_t workspace_bytes,
+                          int32_t topk, int32_t flags, int32_t init_blocks, int32_t local_blocks,
+                          int32_t* topk_ids, void* workspace, size_t workspace_bytes,
                           uint32_t* dev_status, hipStream_t stream) {
   m3s_status st = check_cache(cache);
   if (st != M3S_OK) return st;
@@ -155,6 +156,8 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
   if (st != M3S_OK) return st;
   if (topk < 1 || topk > M3S_MAX_TOPK) return M3S_ERR_UNSUPPORTED;
   if (flags & ~(int32_t)M3S_TOPK_TIE_HIGH_ID) return M3S_ERR_INVALID_ARG;
+  if (init_blocks < 0 || local_blocks < 0 || init_blocks > M3S_MAX_BLOCKS || local_blocks > M3S_MAX_BLOCKS)
+    return M3S_ERR_INVALID_ARG;
   if (rows->num_rows > 0) {
     if (!q_idx || !aligned16(q_idx) || q_idx_stride < M3S_HEAD_DIM || (q_idx_stride & 7)) return M3S_ERR_INVALID_ARG;
     if (!topk_ids) return M3S_ERR_INVALID_ARG;
@@ -180,6 +183,8 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
   a.num_rows = rows->num_rows;
   a.topk = topk;
   a.tie_high = (flags & M3S_TOPK_TIE_HIGH_ID) ? 1 : 0;
+  a.init_blocks = init_blocks;
+  a.local_blocks = local_blocks;
   a.topk_ids = topk_ids;
   a.ws_score = static_cast<float*>(workspace);
   a.ws_bound = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);

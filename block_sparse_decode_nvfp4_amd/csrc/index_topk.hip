@@ -533,18 +533,33 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     if (j >= nb) break;
     pv[i] = btr[j];
   }
+  // forced class of block j: 2 initial, 1 local, 0 scored (initial wins on overlap)
+  const int I = a.init_blocks, L = a.local_blocks;
+  auto cls_of = [&](int j) { return j < I ? 2 : (j >= nb - L ? 1 : 0); };
   // blocks past the row's causal range were never scored: they never compete
-  // and their workspace entries are not read
+  // and their workspace entries are not read; forced blocks' scores play no part
   float dm = 0.f;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
     const int j = tid + 256 * i;
     if (j >= MB) break;
     if (j >= nb) sv[i] = -INFINITY;
-    else dm = fmaxf(dm, bv[i]);
+    else if (cls_of(j) == 0) dm = fmaxf(dm, bv[i]);
   }
-  auto okey = [&](int i) { return ord_f32(sv[i]); };
-  auto ckey = [&](int i) { return comp_key(ord_f32(sv[i]), tid + 256 * i, th); };
+  // ordered keys, formed once: forced blocks above every float (initial
+  // 0xFFFFFFFF, local 0xFFFFFFFE; finite and infinite scores order below
+  // 0xFF800001), ties among them to the higher id
+  uint32_t ok[kSelPer];
+#pragma unroll
+  for (int i = 0; i < kSelPer; ++i) {
+    const int j = tid + 256 * i;
+    if (j >= nb) break;
+    const int c = cls_of(j);
+    ok[i] = c == 2 ? 0xFFFFFFFFu : (c == 1 ? 0xFFFFFFFEu : ord_f32(sv[i]));
+  }
+  auto forced = [&](int i) { return ok[i] >= 0xFFFFFFFEu; };
+  auto okey = [&](int i) { return ok[i]; };
+  auto ckey = [&](int i) { return comp_key(ok[i], tid + 256 * i, forced(i) ? 1 : th); };
 
   // 1. threshold from the per-wave sorted thread maxima
   uint32_t tmax = 0;
@@ -650,7 +665,8 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   // 2. certification
   int mode = 0;  // 0: by key (exact scores); 1: score >= lo; 2: score > hi, band rescored
   double lo = 0.0, hi = 0.0;
-  if (dmax > 0.f) {
+  // when the k-th key is forced, every selected block is forced: keys decide exactly
+  if (dmax > 0.f && (uint32_t)(Kk >> 32) < 0xFFFFFFFEu) {
     lo = (double)unord_f32((uint32_t)(Kk >> 32)) - 2.0 * (double)dmax;
     hi = (double)unord_f32((uint32_t)(K1 >> 32)) + 2.0 * (double)dmax;
     int nin = 0;
@@ -659,7 +675,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       const int j = tid + 256 * i;
       if (j >= nb) break;
       const double s_ = (double)sv[i];
-      if (s_ > hi) {
+      if (forced(i) || s_ > hi) {
         ++nin;
       } else if (s_ >= lo) {
         const int slot = atomicAdd(&sh.cnt[2], 1);
@@ -716,51 +732,62 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
           }
           mx = lane_fmax<1, 64>(mx);
           const double thr = (double)mx - 2.0 * (double)sh.bdel[m];
+          // candidate tokens: bit 4 i + v of lane (0, G) is token 16 i + 4 G + v
+          uint32_t cm = 0;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            uint32_t cm = 0;
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) cm |= ((double)ts[i][v] >= thr ? 1u : 0u) << v;
-            uint64_t holders = __ballot(cm != 0);
-            while (holders) {
-              const int src = __builtin_ctzll(holders);
-              holders &= holders - 1;
-              uint32_t bits = __shfl(cm, src, 64);
-              while (bits) {
-                const int v = __builtin_ctz(bits);
-                bits &= bits - 1;
-                const int nt = 4 * (src >> 4) + v;  // token 16 i + nt of the block
-                const int s2 = nt + 16 * G;         // lane holding dims [32 G, 32 G + 32) of it
-                const uint32_t w0 = __shfl(pb.kr[i][0], s2, 64), w1 = __shfl(pb.kr[i][1], s2, 64);
-                const uint32_t w2 = __shfl(pb.kr[i][2], s2, 64), w3 = __shfl(pb.kr[i][3], s2, 64);
-                const uint32_t sk = __shfl(pb.ks[i], s2, 64);
-                const int ww = (lane & 15) >> 2;
-                const uint32_t word = ww == 0 ? w0 : (ww == 1 ? w1 : (ww == 2 ? w2 : w3));
-                const uint32_t byte = (word >> (8 * (lane & 3))) & 0xFFu;
-                const auto cd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
-                double sd;
-                int lsb;
-                if (FMT == 1) {
-                  const uint32_t sb = (sk >> (8 * ((lane & 15) >> 3))) & 0xFFu;
-                  const uint32_t e = (sb >> 3) & 15u, mm = sb & 7u;
-                  const uint32_t M = e ? (mm | 8u) : mm;
-                  const int ex = e ? (int)e - 10 : -9;
-                  sd = __builtin_ldexp((double)M, ex);
-                  lsb = M ? ex + __builtin_ctz(M) - 1 : INT_MAX;  // codes are multiples of 1/2
-                } else {
-                  sd = __builtin_ldexp(1.0, (int)(sk & 0xFFu) - 127);
-                  lsb = (int)(sk & 0xFFu) - 128;
+            for (int v = 0; v < 4; ++v) cm |= ((double)ts[i][v] >= thr ? 1u : 0u) << (4 * i + v);
+          uint64_t holders = __ballot(cm != 0);
+          while (holders) {
+            const int src = __builtin_ctzll(holders);
+            holders &= holders - 1;
+            uint32_t bits = __shfl(cm, src, 64);
+            while (bits) {
+              const int bit = __builtin_ctz(bits);
+              bits &= bits - 1;
+              const int ti = bit >> 2, v = bit & 3;
+              const int nt = 4 * (src >> 4) + v;  // token 16 ti + nt of the block
+              const int s2 = nt + 16 * G;         // lane holding dims [32 G, 32 G + 32) of it
+              // the tile's words and scales, picked by a select chain (ti is uniform)
+              u32x4 kw = pb.kr[0];
+              uint32_t ksw = pb.ks[0];
+#pragma unroll
+              for (int i = 1; i < 8; ++i) {
+                if (ti == i) {
+                  kw = pb.kr[i];
+                  ksw = pb.ks[i];
                 }
-                const double k0 = (double)cd[0] * sd, k1 = (double)cd[1] * sd;
-                double dot = __builtin_fma(qq.x, k0, qq.y * k1);
-                double mag = __builtin_fma(fabs(qq.x), fabs(k0), fabs(qq.y * k1));
-                dot = lane_reduce<1, 64>(dot, [](double x, double y) { return x + y; });
-                mag = lane_reduce<1, 64>(mag, [](double x, double y) { return x + y; });
-                const int lk = lane_reduce<1, 64>(lsb, [](int x, int y) { return x < y ? x : y; });
-                if (mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
-                  inexact = true;
-                best = fmax(best, dot + 0.0);
               }
+              const uint32_t w0 = __shfl(kw[0], s2, 64), w1 = __shfl(kw[1], s2, 64);
+              const uint32_t w2 = __shfl(kw[2], s2, 64), w3 = __shfl(kw[3], s2, 64);
+              const uint32_t sk = __shfl(ksw, s2, 64);
+              const int ww = (lane & 15) >> 2;
+              const uint32_t word = ww == 0 ? w0 : (ww == 1 ? w1 : (ww == 2 ? w2 : w3));
+              const uint32_t byte = (word >> (8 * (lane & 3))) & 0xFFu;
+              const auto cd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+              double sd;
+              int lsb;
+              if (FMT == 1) {
+                const uint32_t sb = (sk >> (8 * ((lane & 15) >> 3))) & 0xFFu;
+                const uint32_t e = (sb >> 3) & 15u, mm = sb & 7u;
+                const uint32_t M = e ? (mm | 8u) : mm;
+                const int ex = e ? (int)e - 10 : -9;
+                sd = __builtin_ldexp((double)M, ex);
+                lsb = M ? ex + __builtin_ctz(M) - 1 : INT_MAX;  // codes are multiples of 1/2
+              } else {
+                sd = __builtin_ldexp(1.0, (int)(sk & 0xFFu) - 127);
+                lsb = (int)(sk & 0xFFu) - 128;
+              }
+              const double k0 = (double)cd[0] * sd, k1 = (double)cd[1] * sd;
+              double dot = __builtin_fma(qq.x, k0, qq.y * k1);
+              double mag = __builtin_fma(fabs(qq.x), fabs(k0), fabs(qq.y * k1));
+              dot = lane_reduce<1, 64>(dot, [](double x, double y) { return x + y; });
+              mag = lane_reduce<1, 64>(mag, [](double x, double y) { return x + y; });
+              const int lk = lane_reduce<1, 64>(lsb, [](int x, int y) { return x < y ? x : y; });
+              if (mag > 0.0 && lk != INT_MAX && !(mag * (1.0 + 0x1p-40) < __builtin_ldexp(1.0, 53 + lq + lk)))
+                inexact = true;
+              best = fmax(best, dot + 0.0);
             }
           }
         }
@@ -793,8 +820,8 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     if (j >= nb) break;
     bool in;
     if (mode == 0) in = ckey(i) >= Kk;
-    else if (mode == 1) in = (double)sv[i] >= lo;
-    else in = (double)sv[i] > hi;
+    else if (mode == 1) in = forced(i) || (double)sv[i] >= lo;
+    else in = forced(i) || (double)sv[i] > hi;
     if (in) {
       const int slot = atomicAdd(&sh.cnt[3], 1);
       if (slot < 64) sh.sel[slot] = j;

@@ -70,6 +70,8 @@ struct IndexArgs {
   int32_t num_rows;
   int32_t topk;
   int32_t tie_high;
+  int32_t init_blocks;   // forced initial blocks per row
+  int32_t local_blocks;  // forced newest blocks per row
   int32_t* topk_ids;
   float* ws_score;   // [num_rows, max_blocks]
   float* ws_bound;   // [num_rows, max_blocks]

@@ -192,20 +192,28 @@ m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t
  * fewer than k causal blocks. The selection equals the one exact arithmetic
  * makes: the scan computes fp32 scores with a rigorous error bound and
  * rescores, in exact float64, every block whose rank the bound leaves open.
+ * Forced blocks ([VLLM-64198] Design: init / local sentinels on a row's causal
+ * blocks; [ATOM-2744] review notes on init_blocks + local_blocks > topk): the
+ * row's first init_blocks blocks rank above its newest local_blocks blocks,
+ * which rank above every scored block; a block in both sets counts as initial;
+ * ties among forced blocks go to the higher id, so when the forced blocks
+ * exceed k the newest ones (the row's own block among them) are kept.
  *
  *   q_idx        bf16 [num_rows, q_idx_stride] (first 128 used)
  *   block_table  int32 [num_reqs, bt_stride]; block j of request b lives on
  *                page block_table[b * bt_stride + j]
  *   max_blocks   upper bound of ceil(row_len / 128) over rows (<= bt_stride)
  *   topk         in [1, 64]
+ *   flags        0 or M3S_TOPK_TIE_HIGH_ID
+ *   init_blocks, local_blocks  forced block counts, each in [0, M3S_MAX_BLOCKS]
  *   topk_ids     int32 [num_rows, topk] (output); pad rows get -1
  *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_INDEX_TOPK, ...)
  */
 m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
                           const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
-                          const m3s_rows* rows, int32_t topk, int32_t flags, int32_t* topk_ids,
-                          void* workspace, size_t workspace_bytes, uint32_t* dev_status,
-                          hipStream_t stream);
+                          const m3s_rows* rows, int32_t topk, int32_t flags, int32_t init_blocks,
+                          int32_t local_blocks, int32_t* topk_ids, void* workspace,
+                          size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream);
 
 /*
  * m3s_sparse_attend - [ATOM-2746] Summary, Attention: block-sparse attention

@@ -30,7 +30,7 @@ class GpuStep:
 
 
 def run_gpu_step(m3s, cfg, dev, seq_lens=None, q_len=None, G=None, topk=None, fmt=None, flags=0,
-                 sm_scale=None, num_rows=None, case=None, q_idx=None):
+                 sm_scale=None, num_rows=None, case=None, q_idx=None, init_blocks=0, local_blocks=0):
     """Fill the history with m3s_store, then run store / rows / top-k / attend for the step rows."""
     if case is None:
         case = W.make_case(cfg, dev, seq_lens=seq_lens, q_len=q_len, G=G)
@@ -64,7 +64,8 @@ def run_gpu_step(m3s, cfg, dev, seq_lens=None, q_len=None, G=None, topk=None, fm
     if R > qi.shape[0]:   # pad rows: any values
         qi = torch.cat([qi, torch.zeros((R - qi.shape[0], qi.shape[1]), dtype=qi.dtype, device=dev)])
         q = torch.cat([q, torch.zeros((R - q.shape[0],) + tuple(q.shape[1:]), dtype=q.dtype, device=dev)])
-    ids = m3s.m3s_index_topk(cache, qi, bt, lay.max_blocks, rows, topk, flags=flags, dev_status=status)
+    ids = m3s.m3s_index_topk(cache, qi, bt, lay.max_blocks, rows, topk, flags=flags, dev_status=status,
+                             init_blocks=init_blocks, local_blocks=local_blocks)
     out = m3s.m3s_sparse_attend(cache, q, bt, lay.max_blocks, rows, ids, sm_scale, dev_status=status)
     torch.cuda.synchronize()
     return GpuStep(case, cache, rows, ids, out, int(status.item()), bt)
@@ -74,7 +75,8 @@ def _m3s_cache(m3s, fmt, num_pages, dev):
     return m3s.Cache(fmt, num_pages, dev)
 
 
-def oracle_requests(step: GpuStep, fmt, topk, sm_scale, requests, tie_high=False, q_idx_bits=None):
+def oracle_requests(step: GpuStep, fmt, topk, sm_scale, requests, tie_high=False, q_idx_bits=None,
+                    init_blocks=0, local_blocks=0):
     """Oracle ids / outputs for the rows of `requests` (planes quantized by the oracle itself)."""
     case = step.case
     lay = case.layout
@@ -95,7 +97,7 @@ def oracle_requests(step: GpuStep, fmt, topk, sm_scale, requests, tie_high=False
         need = set()
         for r in rows:
             s = P.block_scores(qi[r], kidx, int(row_len[r]))
-            want_ids[r] = P.topk_blocks(s, topk, tie_high)
+            want_ids[r] = P.topk_blocks(s, topk, tie_high, init_blocks, local_blocks)
             need |= {int(j) for j in want_ids[r] if j >= 0}
         kh = np.zeros((n, 128))
         vh = np.zeros((n, 128))

@@ -93,11 +93,11 @@ def test_decode_rows_validation(lib):
 
 
 def _topk(lib, cache=None, q=FAKE, qs=128, bt=FAKE, bts=16, mb=16, rows=None, k=4, flags=0, ids=FAKE,
-          ws=FAKE, wsb=1 << 30):
+          ws=FAKE, wsb=1 << 30, init=0, local=0):
     cache = _cache() if cache is None else cache
     rows = _rows() if rows is None else rows
-    return lib.m3s_index_topk(ctypes.byref(cache), q, qs, bt, bts, mb, ctypes.byref(rows), k, flags, ids,
-                              ws, wsb, None, None)
+    return lib.m3s_index_topk(ctypes.byref(cache), q, qs, bt, bts, mb, ctypes.byref(rows), k, flags, init, local,
+                              ids, ws, wsb, None, None)
 
 
 def test_index_topk_validation(lib):
@@ -106,6 +106,9 @@ def test_index_topk_validation(lib):
     assert _topk(lib, k=0) == E.ERR_UNSUPPORTED
     assert _topk(lib, k=65) == E.ERR_UNSUPPORTED
     assert _topk(lib, flags=2) == E.ERR_INVALID_ARG
+    assert _topk(lib, init=-1) == E.ERR_INVALID_ARG
+    assert _topk(lib, local=-1) == E.ERR_INVALID_ARG
+    assert _topk(lib, init=8193) == E.ERR_INVALID_ARG
     assert _topk(lib, mb=0) == E.ERR_INVALID_ARG
     assert _topk(lib, bts=8, mb=16) == E.ERR_INVALID_ARG
     assert _topk(lib, bts=9000, mb=8193) == E.ERR_UNSUPPORTED

@@ -11,10 +11,11 @@ DEV = torch.device("cuda:0")
 CFG0 = W.config(0)
 
 
-def _check_all(gpu, step, fmt, topk, tie_high=False, q_idx_bits=None):
+def _check_all(gpu, step, fmt, topk, tie_high=False, q_idx_bits=None, init_blocks=0, local_blocks=0):
     lay = step.case.layout
     B = len(lay.seq_lens)
-    ids, _, rr, _ = oracle_requests(step, fmt, topk, 1.0, range(B), tie_high, q_idx_bits)
+    ids, _, rr, _ = oracle_requests(step, fmt, topk, 1.0, range(B), tie_high, q_idx_bits, init_blocks,
+                                    local_blocks)
     got = step.ids.cpu().numpy()
     for r, want in ids.items():
         assert got[r].tolist() == want.tolist(), (r, got[r].tolist(), want.tolist())
@@ -177,3 +178,22 @@ def test_index_adversarial_queries(gpu, fmt):
     step = run_gpu_step(gpu, CFG0, DEV, topk=8, case=case, fmt=fmt, q_idx=qi)
     assert step.status == 0, hex(step.status)
     _check_all(gpu, step, fmt, 8)
+
+
+@pytest.mark.parametrize("init,local,topk", [(1, 2, 8), (4, 16, 16), (0, 3, 4), (20, 0, 16), (3, 3, 4),
+                                             (2, 1, 64)])
+@pytest.mark.parametrize("tie_high", [False, True])
+def test_index_forced_blocks(gpu, init, local, topk, tie_high):
+    """Forced initial / local blocks: ids bit-exact against the oracle on ragged rows, among
+    them the review's case (top-k 16, init 4, local 16) and forced sets larger than k."""
+    seq = [9000, 2048, 700, 129, 40000]
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=seq, q_len=3, G=2, topk=topk, flags=1 if tie_high else 0,
+                        init_blocks=init, local_blocks=local)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, "nvfp4", topk, tie_high, init_blocks=init, local_blocks=local)
+    if (init, local, topk) == (4, 16, 16):
+        ids = step.ids.cpu().numpy()
+        r = int(step.case.layout.cu_q[4]) + 2   # last row of the 40000-token request
+        nb = (40000 + 127) // 128
+        assert ids[r].tolist() == [0, 1, 2, 3] + list(range(nb - 12, nb))
+
