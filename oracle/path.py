@@ -64,6 +64,14 @@ def decode_rows(cu_q, seq_lens, num_rows):
     return row_req, row_len
 
 
+def prefill_rows(cu_q, seq_lens, num_rows):
+    """Prefill rows: every query token of a request's chunk is a row and sees the request's
+    prefix plus the chunk up to itself, the same map as ``decode_rows`` with no bound on a
+    request's row count (the pages' prefill_rows, ATOM PR "[MiniMax-M3.1] FP4 index cache
+    and NVFP4 sparse KV cache", Design: Row maps; "decode_rows / prefill_rows match torch")."""
+    return decode_rows(cu_q, seq_lens, num_rows)
+
+
 def new_planes(fmt: str, num_pages: int):
     """Zeroed plane set {name: (payload [P,128,64], scales [P,128,SB])}."""
     sb = F.scale_bytes(fmt)

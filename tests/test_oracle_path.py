@@ -340,3 +340,25 @@ def test_forced_zero_is_plain_topk_and_short_rows_take_all():
     s = rng.standard_normal(50)
     assert P.topk_blocks(s, 7).tolist() == P.topk_blocks(s, 7, init_blocks=0, local_blocks=0).tolist()
     assert P.topk_blocks(s[:5], 8, init_blocks=3, local_blocks=3).tolist() == [0, 1, 2, 3, 4, -1, -1, -1]
+
+
+def test_prefill_rows_hand_example():
+    """Request 0: prefix 5, chunk 3 (seq 8) -> rows 0-2 see 6, 7, 8 tokens; request 1: no
+    prefix, chunk 40 -> rows 3-42 see 1..40; rows 43, 44 are padding."""
+    rr, rl = P.prefill_rows([0, 3, 43], [8, 40], 45)
+    assert rr.tolist() == [0] * 3 + [1] * 40 + [-1, -1]
+    assert rl.tolist() == [6, 7, 8] + list(range(1, 41)) + [0, 0]
+
+
+def test_prefill_rows_match_searchsorted():
+    """The pages compute prefill rows with searchsorted over the chunk offsets."""
+    rng = np.random.default_rng(4)
+    q = rng.integers(1, 300, 7)
+    cu = np.concatenate([[0], np.cumsum(q)])
+    seq = q + rng.integers(0, 5000, 7)
+    R = int(cu[-1]) + 3
+    rr, rl = P.prefill_rows(cu, seq, R)
+    r = np.arange(int(cu[-1]))
+    b = np.searchsorted(cu, r, side="right") - 1
+    assert np.array_equal(rr[: len(r)], b)
+    assert np.array_equal(rl[: len(r)], seq[b] - (cu[b + 1] - cu[b]) + 1 + (r - cu[b]))
