@@ -6,8 +6,8 @@ current HIP stream) into the C ABI declared in include/m3s.h; every step of
 the path runs in the library's HIP kernels. Loading fails loudly when the
 library is missing: there is no fallback.
 
-Functions carry the C names: m3s_store, m3s_decode_rows, m3s_index_topk,
-m3s_sparse_attend, m3s_workspace_bytes, m3s_read_device_status,
+Functions carry the C names: m3s_store, m3s_decode_rows, m3s_prefill_rows,
+m3s_index_topk, m3s_sparse_attend, m3s_workspace_bytes, m3s_read_device_status,
 m3s_status_string, m3s_version.
 """
 from __future__ import annotations
@@ -32,8 +32,10 @@ DEV_BITS = {
     "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6,
 }
 
-EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_index_topk", "m3s_sparse_attend",
+EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_prefill_rows", "m3s_index_topk", "m3s_sparse_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
+MAX_GROUPS = 4096
+GROUP_ROWS = 16
 
 _c_i32p = ctypes.c_void_p
 _lib = None
@@ -54,8 +56,9 @@ class m3s_cache(ctypes.Structure):
 
 
 class m3s_rows(ctypes.Structure):
-    _fields_ = [("cu_q", ctypes.c_void_p), ("row_req", ctypes.c_void_p), ("row_len", ctypes.c_void_p),
-                ("req_blk", ctypes.c_void_p), ("num_reqs", ctypes.c_int32), ("num_rows", ctypes.c_int32)]
+    _fields_ = [("grp_row", ctypes.c_void_p), ("grp_req", ctypes.c_void_p), ("grp_blk", ctypes.c_void_p),
+                ("row_req", ctypes.c_void_p), ("row_len", ctypes.c_void_p), ("num_groups", ctypes.c_int32),
+                ("num_rows", ctypes.c_int32)]
 
 
 def load(path: str | None = None):
@@ -72,6 +75,7 @@ def load(path: str | None = None):
     sig = {
         "m3s_store": (I32, [V, V, V, V, I64, V, I32, V, V]),
         "m3s_decode_rows": (I32, [V, V, I32, I32, V, V, V, V, V]),
+        "m3s_prefill_rows": (I32, [V, V, I32, I32, I32, V, V, V, V, V, V, V]),
         "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, I32, I32, V, V, SZ, V, V]),
         "m3s_sparse_attend": (I32, [V, V, I64, I64, I32, V, I32, I32, V, V, I32, F32, V, V, SZ, V, V]),
         "m3s_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
@@ -156,13 +160,20 @@ class Cache:
 
 
 class Rows:
-    """The row map of one step (device tensors) and its m3s_rows struct."""
+    """The row map of one step and the index scan's work groups (device tensors), with
+    their m3s_rows struct. From m3s_decode_rows: one group per request (grp_row = cu_q,
+    grp_req None); from m3s_prefill_rows: 16-row groups."""
 
-    def __init__(self, cu_q, row_req, row_len, req_blk, num_reqs: int, num_rows: int):
-        self.cu_q, self.row_req, self.row_len, self.req_blk = cu_q, row_req, row_len, req_blk
-        self.num_reqs, self.num_rows = int(num_reqs), int(num_rows)
-        self.c = m3s_rows(cu_q.data_ptr(), row_req.data_ptr(), row_len.data_ptr(), req_blk.data_ptr(),
-                          self.num_reqs, self.num_rows)
+    def __init__(self, grp_row, grp_req, grp_blk, row_req, row_len, num_groups: int, num_rows: int):
+        self.grp_row, self.grp_req, self.grp_blk = grp_row, grp_req, grp_blk
+        self.row_req, self.row_len = row_req, row_len
+        self.num_groups, self.num_rows = int(num_groups), int(num_rows)
+        self.c = m3s_rows(grp_row.data_ptr(), None if grp_req is None else grp_req.data_ptr(), grp_blk.data_ptr(),
+                          row_req.data_ptr(), row_len.data_ptr(), self.num_groups, self.num_rows)
+
+    @property
+    def num_reqs(self):
+        return self.num_groups
 
     def ref(self):
         return ctypes.byref(self.c)
@@ -202,7 +213,32 @@ def m3s_decode_rows(cu_q, seq_lens, num_rows: int, row_req=None, row_len=None, r
     st = load().m3s_decode_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, _ptr(row_req), _ptr(row_len),
                                 _ptr(req_blk), _ptr(dev_status), _stream(stream))
     _check("m3s_decode_rows", st)
-    return Rows(cu_q, row_req, row_len, req_blk, B, num_rows)
+    return Rows(cu_q, None, req_blk, row_req, row_len, B, num_rows)
+
+
+def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = None, dev_status=None,
+                     stream=None) -> Rows:
+    """Prefill row map and 16-row scan groups; max_groups defaults to the bound
+    ceil(num_rows / 16) + num_reqs (capped at MAX_GROUPS)."""
+    torch = _torch()
+    _need(cu_q, "cu_q", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    B = seq_lens.numel()
+    if cu_q.numel() != B + 1:
+        raise ValueError("cu_q must have num_reqs + 1 entries")
+    if max_groups is None:
+        max_groups = min(MAX_GROUPS, max(1, (num_rows + GROUP_ROWS - 1) // GROUP_ROWS + B))
+    dev = cu_q.device
+    row_req = torch.empty(num_rows, dtype=torch.int32, device=dev)
+    row_len = torch.empty(num_rows, dtype=torch.int32, device=dev)
+    grp_row = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
+    grp_req = torch.empty(max_groups, dtype=torch.int32, device=dev)
+    grp_blk = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
+    st = load().m3s_prefill_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, max_groups, _ptr(row_req),
+                                 _ptr(row_len), _ptr(grp_row), _ptr(grp_req), _ptr(grp_blk), _ptr(dev_status),
+                                 _stream(stream))
+    _check("m3s_prefill_rows", st)
+    return Rows(grp_row, grp_req, grp_blk, row_req, row_len, max_groups, num_rows)
 
 
 def index_workspace(rows: Rows, max_blocks: int, topk: int, device="cuda"):

@@ -28,9 +28,9 @@ m3s_status check_cache(const m3s_cache* c) {
 
 m3s_status check_rows(const m3s_rows* r) {
   if (!r) return M3S_ERR_INVALID_ARG;
-  if (r->num_reqs < 0 || r->num_rows < 0) return M3S_ERR_INVALID_ARG;
-  if (r->num_reqs > M3S_MAX_REQS || r->num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
-  if (!r->cu_q || !r->req_blk) return M3S_ERR_INVALID_ARG;
+  if (r->num_groups < 0 || r->num_rows < 0) return M3S_ERR_INVALID_ARG;
+  if (r->num_groups > M3S_MAX_GROUPS || r->num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
+  if (!r->grp_row || !r->grp_blk) return M3S_ERR_INVALID_ARG;
   if (r->num_rows > 0 && (!r->row_req || !r->row_len)) return M3S_ERR_INVALID_ARG;
   return M3S_OK;
 }
@@ -138,8 +138,35 @@ m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t
   a.row_req = row_req;
   a.row_len = row_len;
   a.req_blk = req_blk;
+  a.grp_row = nullptr;
+  a.grp_req = nullptr;
+  a.max_groups = 0;
   a.status = dev_status;
   return from_hip(launch_decode_rows(a, stream));
+}
+
+m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
+                            int32_t max_groups, int32_t* row_req, int32_t* row_len, int32_t* grp_row,
+                            int32_t* grp_req, int32_t* grp_blk, uint32_t* dev_status, hipStream_t stream) {
+  if (num_reqs < 0 || num_rows < 0) return M3S_ERR_INVALID_ARG;
+  if (num_reqs > M3S_MAX_REQS || num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
+  if (max_groups < 1 || max_groups > M3S_MAX_GROUPS) return M3S_ERR_UNSUPPORTED;
+  if (!cu_q || !grp_row || !grp_req || !grp_blk) return M3S_ERR_INVALID_ARG;
+  if (num_reqs > 0 && !seq_lens) return M3S_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!row_req || !row_len)) return M3S_ERR_INVALID_ARG;
+  RowsArgs a;
+  a.cu_q = cu_q;
+  a.seq_lens = seq_lens;
+  a.num_reqs = num_reqs;
+  a.num_rows = num_rows;
+  a.row_req = row_req;
+  a.row_len = row_len;
+  a.req_blk = grp_blk;
+  a.grp_row = grp_row;
+  a.grp_req = grp_req;
+  a.max_groups = max_groups;
+  a.status = dev_status;
+  return from_hip(launch_prefill_rows(a, stream));
 }
 
 m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
@@ -175,11 +202,12 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
   a.block_table = block_table;
   a.bt_stride = bt_stride;
   a.max_blocks = max_blocks;
-  a.cu_q = rows->cu_q;
+  a.cu_q = rows->grp_row;
+  a.grp_req = rows->grp_req;
   a.row_req = rows->row_req;
   a.row_len = rows->row_len;
-  a.req_blk = rows->req_blk;
-  a.num_reqs = rows->num_reqs;
+  a.req_blk = rows->grp_blk;
+  a.num_reqs = rows->num_groups;
   a.num_rows = rows->num_rows;
   a.topk = topk;
   a.tie_high = (flags & M3S_TOPK_TIE_HIGH_ID) ? 1 : 0;

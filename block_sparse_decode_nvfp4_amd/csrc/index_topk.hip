@@ -374,7 +374,8 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a
       int key = -1, pg = -1;
       if (jl < a.max_blocks) {
         key = bl * kMaxBlocks + jl;
-        pg = a.block_table[(int64_t)bl * a.bt_stride + jl];
+        const int breq = a.grp_req ? a.grp_req[bl] : bl;  // the group's request
+        pg = breq >= 0 ? a.block_table[(int64_t)breq * a.bt_stride + jl] : -1;
         if (pg < 0 || pg >= a.num_pages) {
           set_status(a.status, kDevBadPage);
           pg = -1;

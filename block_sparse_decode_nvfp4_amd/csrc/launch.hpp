@@ -48,7 +48,10 @@ struct RowsArgs {
   int32_t num_rows;
   int32_t* row_req;
   int32_t* row_len;
-  int32_t* req_blk;
+  int32_t* req_blk;   // decode_rows: block prefix per request; prefill_rows: per group
+  int32_t* grp_row;   // prefill_rows only: [max_groups + 1]
+  int32_t* grp_req;   // prefill_rows only: [max_groups]
+  int32_t max_groups; // prefill_rows only
   uint32_t* status;
 };
 
@@ -62,7 +65,8 @@ struct IndexArgs {
   const int32_t* block_table;
   int32_t bt_stride;
   int32_t max_blocks;
-  const int32_t* cu_q;
+  const int32_t* cu_q;     // first row of each scan work group [num_reqs + 1]
+  const int32_t* grp_req;  // request of each work group, or null: group g is request g
   const int32_t* row_req;
   const int32_t* row_len;
   const int32_t* req_blk;
@@ -108,6 +112,7 @@ struct AttendArgs {
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows(const RowsArgs& a, hipStream_t stream);
+hipError_t launch_prefill_rows(const RowsArgs& a, hipStream_t stream);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);
 

@@ -66,6 +66,7 @@ extern "C" {
 #define M3S_MAX_HEADS 16     /* query heads per KV head (G) */
 #define M3S_MAX_TOPK 64
 #define M3S_MAX_REQS 4096
+#define M3S_MAX_GROUPS 4096  /* scan work groups (requests, or 16-row prefill groups) */
 #define M3S_MAX_ROWS 65536
 #define M3S_MAX_BLOCKS 8192  /* causal blocks per request: 1,048,576 tokens */
 
@@ -88,7 +89,7 @@ enum {
 /* Sticky device status bits (ORed into *dev_status). */
 enum {
   M3S_DEV_BAD_SLOT = 1u << 0,     /* store: slot >= num_pages * 128 */
-  M3S_DEV_BAD_ROWS = 1u << 1,     /* decode_rows: q_len outside [1, 16], seq_len < q_len,
+  M3S_DEV_BAD_ROWS = 1u << 1,     /* decode_rows / prefill_rows: q_len outside its range, seq_len < q_len,
                                      cu_q not non-decreasing, or cu_q[B] > num_rows */
   M3S_DEV_BAD_LENGTH = 1u << 2,   /* a live row needs more than max_blocks blocks */
   M3S_DEV_BAD_PAGE = 1u << 3,     /* block table entry outside [0, num_pages) */
@@ -133,17 +134,23 @@ typedef struct m3s_cache {
 
 /*
  * The row map of one step (host struct of device pointers), filled by
- * m3s_decode_rows and shared by m3s_index_topk and m3s_sparse_attend
- * ([ATOM-2744] Design, Attention: one decode_rows launch, shared by the
- * attention and the fused top-k).
+ * m3s_decode_rows or m3s_prefill_rows and shared by m3s_index_topk and
+ * m3s_sparse_attend ([ATOM-2744] Design, Attention: one row-map launch,
+ * shared by the attention and the fused top-k).
+ *
+ * The index scan scores one page against a work group of at most 16
+ * consecutive rows of one request at a time. m3s_decode_rows makes each
+ * request one group (grp_row = cu_q, grp_req = NULL); m3s_prefill_rows cuts a
+ * request's rows into groups of 16.
  */
 typedef struct m3s_rows {
-  const int32_t* cu_q;    /* [num_reqs + 1] first row of each request (input of decode_rows) */
+  const int32_t* grp_row; /* [num_groups + 1] first row of each work group; grp_row[num_groups] ends the rows */
+  const int32_t* grp_req; /* [num_groups] request of each group (-1: empty), or NULL: group g is request g */
+  const int32_t* grp_blk; /* [num_groups + 1] exclusive prefix sum of each group's causal block count */
   const int32_t* row_req; /* [num_rows] request of each row, -1 for a pad row */
   const int32_t* row_len; /* [num_rows] causal length of each row, 0 for a pad row */
-  const int32_t* req_blk; /* [num_reqs + 1] exclusive prefix sum of ceil(seq_len / 128) */
-  int32_t num_reqs;
-  int32_t num_rows;       /* padded row count (>= cu_q[num_reqs]) */
+  int32_t num_groups;     /* <= M3S_MAX_GROUPS */
+  int32_t num_rows;       /* padded row count */
 } m3s_rows;
 
 /*
@@ -175,11 +182,33 @@ m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* 
  *   cu_q       int32 [num_reqs + 1], seq_lens int32 [num_reqs]
  *   row_req, row_len  int32 [num_rows] (outputs), req_blk int32 [num_reqs + 1] (output)
  * A request with q_len outside [1, 16] or seq_len < q_len sets M3S_DEV_BAD_ROWS
- * and its rows become pad rows (its block count is 0).
+ * and its rows become pad rows (its block count is 0). For m3s_index_topk and
+ * m3s_sparse_attend, pass m3s_rows { grp_row = cu_q, grp_req = NULL,
+ * grp_blk = req_blk, row_req, row_len, num_groups = num_reqs, num_rows }.
  */
 m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs,
                            int32_t num_rows, int32_t* row_req, int32_t* row_len,
                            int32_t* req_blk, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * m3s_prefill_rows - [ATOM-2744] Design, row maps (prefill_rows): every query
+ * token of a request's prefill chunk is a row; row r of request b sees
+ *   row_len = seq_lens[b] - (cu_q[b+1] - cu_q[b]) + 1 + (r - cu_q[b])
+ * tokens (the decode_rows map with no bound on a request's row count). It
+ * also cuts each request's rows into work groups of 16 for the index scan:
+ *   grp_row int32 [max_groups + 1], grp_req int32 [max_groups],
+ *   grp_blk int32 [max_groups + 1] (outputs; groups past the last real one
+ *   are empty); pass them with num_groups = max_groups in m3s_rows.
+ *   max_groups   in [1, M3S_MAX_GROUPS]; sum_b ceil(q_len_b / 16) groups are
+ *                needed, at most ceil(cu_q[B] / 16) + num_reqs
+ * A request with seq_len < q_len sets M3S_DEV_BAD_ROWS and its rows become pad
+ * rows. A cu_q that does not start at 0, decreases or passes num_rows, or more
+ * groups than max_groups, sets M3S_DEV_BAD_ROWS and makes every row a pad row.
+ */
+m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs,
+                            int32_t num_rows, int32_t max_groups, int32_t* row_req, int32_t* row_len,
+                            int32_t* grp_row, int32_t* grp_req, int32_t* grp_blk, uint32_t* dev_status,
+                            hipStream_t stream);
 
 /*
  * m3s_index_topk - [ATOM-2744] Design, Index and Decode score grid, and Fused

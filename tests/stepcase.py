@@ -30,7 +30,8 @@ class GpuStep:
 
 
 def run_gpu_step(m3s, cfg, dev, seq_lens=None, q_len=None, G=None, topk=None, fmt=None, flags=0,
-                 sm_scale=None, num_rows=None, case=None, q_idx=None, init_blocks=0, local_blocks=0):
+                 sm_scale=None, num_rows=None, case=None, q_idx=None, init_blocks=0, local_blocks=0,
+                 prefill=False):
     """Fill the history with m3s_store, then run store / rows / top-k / attend for the step rows."""
     if case is None:
         case = W.make_case(cfg, dev, seq_lens=seq_lens, q_len=q_len, G=G)
@@ -57,7 +58,10 @@ def run_gpu_step(m3s, cfg, dev, seq_lens=None, q_len=None, G=None, topk=None, fm
     m3s.m3s_store(cache, case.k[new_idx], case.v[new_idx], case.idx[new_idx], slots[new_idx].contiguous(), status)
     cu_q = torch.as_tensor(lay.cu_q, device=dev)
     seq = torch.as_tensor(lay.seq_lens, device=dev)
-    rows = m3s.m3s_decode_rows(cu_q, seq, R, dev_status=status)
+    if prefill:
+        rows = m3s.m3s_prefill_rows(cu_q, seq, R, dev_status=status)
+    else:
+        rows = m3s.m3s_decode_rows(cu_q, seq, R, dev_status=status)
     bt = torch.as_tensor(lay.block_table, device=dev)
     qi = case.q_idx
     q = case.q

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
-    for n in ("m3s_store", "m3s_decode_rows", "m3s_index_topk", "m3s_sparse_attend"):
+    for n in ("m3s_store", "m3s_decode_rows", "m3s_prefill_rows", "m3s_index_topk", "m3s_sparse_attend"):
         assert n in names
     assert set(names) == set(m3s.EXPORTS)
 
@@ -51,7 +51,7 @@ def _cache(fmt=1, pages=4, page=128, dim=128, heads=1, ptr=4096):
 
 
 def _rows(nreq=1, nrows=1, ptr=4096):
-    return m3s.m3s_rows(ptr, ptr, ptr, ptr, nreq, nrows)
+    return m3s.m3s_rows(ptr, None, ptr, ptr, ptr, nreq, nrows)
 
 
 FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first or the call is not made
@@ -161,3 +161,22 @@ def test_workspace_sizes_scale_with_shape(lib):
     assert b >= 64 * 4 * 16 * 128 * 4
     assert m3s.m3s_workspace_bytes(99, 1, 1, 1, 1, 1) == 0
     assert m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 1, 1, 1, 0, 1) == 0
+
+
+def test_prefill_rows_validation(lib):
+    f = lambda cu=FAKE, seq=FAKE, B=1, R=1, G=4, rr=FAKE, rl=FAKE, gr=FAKE, gq=FAKE, gb=FAKE: lib.m3s_prefill_rows(
+        cu, seq, B, R, G, rr, rl, gr, gq, gb, None, None)
+    E = m3s
+    assert f(B=-1) == E.ERR_INVALID_ARG
+    assert f(R=-1) == E.ERR_INVALID_ARG
+    assert f(B=4097) == E.ERR_UNSUPPORTED
+    assert f(R=65537) == E.ERR_UNSUPPORTED
+    assert f(G=0) == E.ERR_UNSUPPORTED
+    assert f(G=4097) == E.ERR_UNSUPPORTED
+    assert f(cu=None) == E.ERR_INVALID_ARG
+    assert f(seq=None) == E.ERR_INVALID_ARG
+    assert f(gr=None) == E.ERR_INVALID_ARG
+    assert f(gq=None) == E.ERR_INVALID_ARG
+    assert f(gb=None) == E.ERR_INVALID_ARG
+    assert f(rr=None) == E.ERR_INVALID_ARG
+

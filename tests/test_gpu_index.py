@@ -197,3 +197,25 @@ def test_index_forced_blocks(gpu, init, local, topk, tie_high):
         nb = (40000 + 127) // 128
         assert ids[r].tolist() == [0, 1, 2, 3] + list(range(nb - 12, nb))
 
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_prefill_step(gpu, fmt):
+    """Prefill rows (chunks of 300, 40 and 133 tokens after prefixes, and a 700-token
+    request with no prefix) through the same scan, top-k and attention: ids bit-exact,
+    attention within 5e-3 on every row."""
+    from tests.stepcase import max_rel_err
+    seq = [3300, 700, 1500, 173]
+    ql = [300, 700, 40, 133]
+    case = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=4)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=8, case=case, fmt=fmt, prefill=True, sm_scale=0.3)
+    assert step.status == 0, hex(step.status)
+    ids, outs, rr, rl = oracle_requests(step, fmt, 8, 0.3, range(len(seq)))
+    got = step.ids.cpu().numpy()
+    o = step.out.cpu().double().numpy()
+    assert np.array_equal(step.rows.row_req.cpu().numpy(), rr)
+    worst = 0.0
+    for r, want in ids.items():
+        assert got[r].tolist() == want.tolist(), (r, got[r].tolist(), want.tolist())
+        worst = max(worst, max_rel_err(o[r], outs[r]))
+    assert worst <= 5e-3, worst

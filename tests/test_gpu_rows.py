@@ -14,7 +14,7 @@ def _run(m3s, cu_q, seq, R):
     rows = m3s.m3s_decode_rows(torch.as_tensor(np.asarray(cu_q, np.int32), device=DEV),
                                torch.as_tensor(np.asarray(seq, np.int32), device=DEV), R, dev_status=st)
     torch.cuda.synchronize()
-    return rows.row_req.cpu().numpy(), rows.row_len.cpu().numpy(), rows.req_blk.cpu().numpy(), int(st.item())
+    return rows.row_req.cpu().numpy(), rows.row_len.cpu().numpy(), rows.grp_blk.cpu().numpy(), int(st.item())
 
 
 def test_rows_random_batches(gpu):
@@ -50,3 +50,67 @@ def test_rows_reject_bad_requests(gpu):
 def test_rows_empty_batch(gpu):
     rr, rl, rb, st = _run(gpu, [0], np.zeros(0, np.int32), 5)
     assert st == 0 and np.all(rr == -1) and np.all(rl == 0) and rb.tolist() == [0]
+
+
+def _prefill(m3s, cu_q, seq, R, max_groups=None):
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rows = m3s.m3s_prefill_rows(torch.as_tensor(np.asarray(cu_q, np.int32), device=DEV),
+                                torch.as_tensor(np.asarray(seq, np.int32), device=DEV), R, max_groups, dev_status=st)
+    torch.cuda.synchronize()
+    g = lambda t: t.cpu().numpy()
+    return g(rows.row_req), g(rows.row_len), g(rows.grp_row), g(rows.grp_req), g(rows.grp_blk), int(st.item())
+
+
+def _check_groups(cu, seq, rl, gr, gq, gb):
+    """Work groups: consecutive runs of at most 16 rows of one request, in row order,
+    covering every live row once; block prefix = causal blocks of each group's last row."""
+    G = len(gq)
+    live = [g for g in range(G) if gq[g] >= 0]
+    want_rows, nb = [], []
+    for b in range(len(seq)):
+        for s0 in range(int(cu[b]), int(cu[b + 1]), 16):
+            want_rows.append((s0, b))
+    assert [(int(gr[g]), int(gq[g])) for g in live] == want_rows
+    assert live == list(range(len(live)))                  # real groups first
+    for g in range(G):
+        n = int(gr[g + 1] - gr[g])
+        if gq[g] >= 0:
+            b = int(gq[g])
+            assert 1 <= n <= 16 and gr[g] >= cu[b] and gr[g + 1] <= cu[b + 1]
+            nb.append((int(rl[gr[g + 1] - 1]) + 127) // 128 if seq[b] >= cu[b + 1] - cu[b] else 0)
+        else:
+            assert n == 0
+            nb.append(0)
+    assert np.array_equal(gb, np.concatenate([[0], np.cumsum(nb)]))
+
+
+def test_prefill_rows_random_batches(gpu):
+    rng = np.random.default_rng(9)
+    for B, qmax in ((1, 3000), (3, 700), (8, 40), (50, 300), (200, 20)):
+        ql = rng.integers(1, qmax + 1, size=B)
+        seq = ql + rng.integers(0, 200_000, size=B)
+        cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        R = int(cu[-1]) + int(rng.integers(0, 40))
+        if R > 65536:
+            continue
+        rr, rl, gr, gq, gb, st = _prefill(gpu, cu, seq, R)
+        wr, wl = P.prefill_rows(cu, seq, R)
+        assert st == 0
+        assert np.array_equal(rr, wr) and np.array_equal(rl, wl), B
+        _check_groups(cu, seq, rl, gr, gq, gb)
+
+
+def test_prefill_rows_reject(gpu):
+    bad_bit = gpu.DEV_BITS["BAD_ROWS"]
+    # a request with seq_len < q_len: its rows are pad rows, the others are mapped
+    cu, seq = [0, 40, 45, 80], [100, 3, 35]
+    rr, rl, gr, gq, gb, st = _prefill(gpu, cu, seq, 80)
+    assert st & bad_bit
+    assert np.all(rr[40:45] == -1) and np.all(rl[40:45] == 0)
+    assert rr[:40].tolist() == [0] * 40 and rl[79] == 35
+    _check_groups(cu, seq, rl, gr, gq, gb)
+    # a decreasing cu_q, or too few groups: every row becomes a pad row
+    for cu, seq, R, G in (([0, 30, 20, 50], [30, 40, 50], 50, None), ([0, 40, 80], [40, 80], 80, 4)):
+        rr, rl, gr, gq, gb, st = _prefill(gpu, cu, seq, R, G)
+        assert st & bad_bit
+        assert np.all(rr == -1) and np.all(rl == 0) and gb[-1] == 0 and np.all(gq == -1)

@@ -113,9 +113,10 @@ class Layout:
 
 
 def make_layout(seq_lens, q_len, seed: int, spare_pages: int = 0) -> Layout:
+    """q_len: rows per request, one value for all or one per request (prefill chunks)."""
     seq = np.asarray(seq_lens, dtype=np.int64)
     B = len(seq)
-    ql = np.full(B, q_len, dtype=np.int32)
+    ql = np.broadcast_to(np.asarray(q_len, dtype=np.int32), (B,)).copy()
     if np.any(seq < ql):
         raise ValueError("seq_len must be >= q_len")
     nblk = (seq + PAGE - 1) // PAGE
@@ -134,8 +135,8 @@ def make_layout(seq_lens, q_len, seed: int, spare_pages: int = 0) -> Layout:
     tok_off[1:] = np.cumsum(seq)
     new_tok, new_slot = [], []
     for b in range(B):
-        for i in range(q_len):
-            t = int(seq[b]) - q_len + i
+        for i in range(int(ql[b])):
+            t = int(seq[b]) - int(ql[b]) + i
             new_tok.append(int(tok_off[b]) + t)
             new_slot.append(int(bt[b, t // PAGE]) * PAGE + t % PAGE)
     return Layout(seq.astype(np.int32), ql, cu_q, nblk.astype(np.int32), bt, num_pages,
@@ -207,7 +208,7 @@ def make_case(cfg: Config, device="cpu", seq_lens=None, q_len=None, G=None) -> C
     g = cfg.G if G is None else G
     lay = make_layout(seq, ql, cfg.seed)
     n = lay.total_tokens
-    R = len(seq) * ql
+    R = int(lay.cu_q[-1])
     k = gen_rows(n, cfg.seed, K_FAMILY, device)
     v = gen_rows(n, cfg.seed, V_FAMILY, device)
     idx = gen_rows(n, cfg.seed, IDX_FAMILY, device)
