@@ -217,9 +217,10 @@ def m3s_decode_rows(cu_q, seq_lens, num_rows: int, row_req=None, row_len=None, r
 
 
 def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = None, dev_status=None,
-                     stream=None) -> Rows:
+                     stream=None, out: Rows | None = None) -> Rows:
     """Prefill row map and 16-row scan groups; max_groups defaults to the bound
-    ceil(num_rows / 16) + num_reqs (capped at MAX_GROUPS)."""
+    ceil(num_rows / 16) + num_reqs (capped at MAX_GROUPS). ``out`` (a Rows from an
+    earlier call with the same sizes) is written in place."""
     torch = _torch()
     _need(cu_q, "cu_q", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
@@ -229,16 +230,21 @@ def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = Non
     if max_groups is None:
         max_groups = min(MAX_GROUPS, max(1, (num_rows + GROUP_ROWS - 1) // GROUP_ROWS + B))
     dev = cu_q.device
-    row_req = torch.empty(num_rows, dtype=torch.int32, device=dev)
-    row_len = torch.empty(num_rows, dtype=torch.int32, device=dev)
-    grp_row = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
-    grp_req = torch.empty(max_groups, dtype=torch.int32, device=dev)
-    grp_blk = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
+    if out is not None:
+        if out.num_groups != max_groups or out.num_rows != num_rows:
+            raise ValueError("out was made for other sizes")
+        row_req, row_len, grp_row, grp_req, grp_blk = out.row_req, out.row_len, out.grp_row, out.grp_req, out.grp_blk
+    else:
+        row_req = torch.empty(num_rows, dtype=torch.int32, device=dev)
+        row_len = torch.empty(num_rows, dtype=torch.int32, device=dev)
+        grp_row = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
+        grp_req = torch.empty(max_groups, dtype=torch.int32, device=dev)
+        grp_blk = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
     st = load().m3s_prefill_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, max_groups, _ptr(row_req),
                                  _ptr(row_len), _ptr(grp_row), _ptr(grp_req), _ptr(grp_blk), _ptr(dev_status),
                                  _stream(stream))
     _check("m3s_prefill_rows", st)
-    return Rows(grp_row, grp_req, grp_blk, row_req, row_len, max_groups, num_rows)
+    return out if out is not None else Rows(grp_row, grp_req, grp_blk, row_req, row_len, max_groups, num_rows)
 
 
 def index_workspace(rows: Rows, max_blocks: int, topk: int, device="cuda"):

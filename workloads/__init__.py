@@ -77,6 +77,9 @@ CONFIGS = (
            description="48 requests x 8 rows, lognormal contexts (median 160K, sigma 0.5, clip 16K..450K)"),
     Config(4, "b8x8_150k_mxfp4", (150_000,) * 8, 8, 16, 16, "mxfp4",
            description="config b8x8_150k with MXFP4 planes (E8M0 scale per 32)"),
+    Config(5, "prefill_1x4096_150k", (150_000,), 4096, 16, 16, "nvfp4",
+           description="prefill: one request, a 4096-token chunk after a 145,904-token prefix, G=16, "
+                       "top-k 16, NVFP4"),
 )
 
 
