@@ -219,3 +219,12 @@ def test_prefill_step(gpu, fmt):
         assert got[r].tolist() == want.tolist(), (r, got[r].tolist(), want.tolist())
         worst = max(worst, max_rel_err(o[r], outs[r]))
     assert worst <= 5e-3, worst
+
+
+@pytest.mark.parametrize("topk", [16, 64])
+def test_index_max_blocks(gpu, topk):
+    """The largest rows: one request of 1,000,000 tokens (7813 blocks, the select's widest
+    variant), two rows; ids bit-exact against the oracle."""
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=[1_000_000], q_len=2, G=2, topk=topk)
+    assert step.status == 0, hex(step.status)
+    _check_all(gpu, step, "nvfp4", topk)
