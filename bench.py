@@ -179,7 +179,9 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--cpu-requests", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--stage-reps", type=int, default=50)
+    ap.add_argument("--stage-reps", type=int, default=20)
+    ap.add_argument("--separate", action="store_true",
+                    help="call m3s_store and m3s_decode_rows separately (default: m3s_store_and_rows, one launch)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB float32 copy kernel (torch.neg) whose HBM bytes are known, "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -257,21 +259,16 @@ def main():
     ws_i = m3s.index_workspace(rows, lay.max_blocks, cfg.topk, dev)
     ws_a = m3s.attend_workspace(rows, lay.max_blocks, cfg.topk, G, dev)
 
-    def run_step(c, evs=None):
-        if evs:
-            evs[0].record()
-        m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
-        if evs:
-            evs[1].record()
-        row_map()
-        if evs:
-            evs[2].record()
+    fused_front = not prefill and not args.separate
+
+    def run_step(c):
+        if fused_front:
+            m3s.m3s_store_and_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, row_req, row_len, req_blk, status)
+        else:
+            m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
+            row_map()
         m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0, ids, ws_i, status)
-        if evs:
-            evs[3].record()
         m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids, cfg.sm_scale, out, ws_a, status)
-        if evs:
-            evs[4].record()
 
     for c in caches:  # eager warm-up, checks the status word
         run_step(c)
@@ -320,21 +317,39 @@ def main():
     st = int(status.item())
 
     # ---- per-stage HIP-event times. Events cannot be recorded inside a captured graph on
-    # ROCm, so the stages are launched eagerly on the same stream with events between
-    # them; a GPU spin first lets every launch queue up before the GPU reaches it, so no
-    # host launch gap lands between two events.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
-    acc = np.zeros(4)
-    n = 0
-    for rep in range(max(1, args.stage_reps // 10)):
-        torch.cuda._sleep(3_000_000)
-        for i in range(10):
-            run_step(caches[(rep * 10 + i + 1) % NL], evs[i])
-        torch.cuda.synchronize()
-        for i in range(10):
-            acc += [evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
-            n += 1
-    stage_ms = (acc / n).tolist()
+    # ROCm, so each stage is launched eagerly, args.stage_reps times back to back (cycling
+    # the layer caches), between two events on the stream it runs on; a GPU spin first lets
+    # every launch queue up before the GPU reaches it, so no host launch gap lands inside
+    # and the events' own cost is spread over the repetitions.
+    def front(c):
+        if fused_front:
+            m3s.m3s_store_and_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, row_req, row_len, req_blk, status)
+        else:
+            m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
+            row_map()
+
+    stages = [("store_and_rows" if fused_front else ("store+prefill_rows" if prefill else "store+decode_rows"), front),
+              ("index_topk", lambda c: m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0,
+                                                           ids, ws_i, status)),
+              ("sparse_attend", lambda c: m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids,
+                                                                 cfg.sm_scale, out, ws_a, status))]
+    reps = max(1, args.stage_reps)
+    stage_ms = []
+    for _, fn in stages:
+        best = None
+        for trial in range(3):
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(3_000_000)
+            ea.record()
+            for i in range(reps):
+                fn(caches[(trial * reps + i + 1) % NL])
+            eb.record()
+            torch.cuda.synchronize()
+            t = ea.elapsed_time(eb) / reps
+            best = t if best is None else min(best, t)
+        stage_ms.append(best)
+
     st = st | int(status.item())
 
     ids_np = ids.cpu().numpy()
@@ -346,9 +361,10 @@ def main():
         f"other {by['other'] / 1e6:.2f} MB, total {by['total'] / 1e6:.2f} MB -> {gbs_step:.0f} GB/s")
     roofline = None
     if stage_ms:
-        names = ["store", "prefill_rows" if prefill else "decode_rows", "index_topk", "sparse_attend"]
-        log("[bench] stages (us): " + ", ".join(f"{nm} {v * 1e3:.2f}" for nm, v in zip(names, stage_ms)))
-        t_idx = stage_ms[2] / 1e3
+        names = [nm for nm, _ in stages]
+        log("[bench] stages (us, each stage launched back to back): " +
+            ", ".join(f"{nm} {v * 1e3:.2f}" for nm, v in zip(names, stage_ms)))
+        t_idx = stage_ms[1] / 1e3
         ach = by["index_call"] / t_idx / 1e9
         traffic = None
         if os.path.exists(TRAFFIC_FILE):
@@ -361,7 +377,7 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "m3s_index_topk (index_scan + index_select kernels)",
-                    "launch_us": round(stage_ms[2] * 1e3, 2), "bytes_per_launch": by["index_call"]}
+                    "launch_us": round(stage_ms[1] * 1e3, 2), "bytes_per_launch": by["index_call"]}
 
     cpu = None
     if not args.no_cpu and not prefill:  # the oracle on a 4096-row chunk takes hours
@@ -384,10 +400,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "requests": len(lay.seq_lens), "rows_per_request": cfg.q_len,
                    "context": [int(x) for x in sorted(set(lay.seq_lens.tolist()))][:4],
-                   "heads_per_kv_head": G, "topk": cfg.topk, "cache_format": cfg.fmt, "layers_cycled": NL},
+                   "heads_per_kv_head": G, "topk": cfg.topk, "cache_format": cfg.fmt, "layers_cycled": NL,
+                   "front": "m3s_store_and_rows" if fused_front else "separate store and row-map calls"},
         "hbm_gbs_step": round(gbs_step, 1),
         "bytes_per_step": by["total"],
-        "stage_us": None if not stage_ms else [round(v * 1e3, 2) for v in stage_ms],
+        "stage_us": None if not stage_ms else {nm: round(v * 1e3, 2) for (nm, _), v in zip(stages, stage_ms)},
         "device_status": st,
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -6,7 +6,7 @@ current HIP stream) into the C ABI declared in include/m3s.h; every step of
 the path runs in the library's HIP kernels. Loading fails loudly when the
 library is missing: there is no fallback.
 
-Functions carry the C names: m3s_store, m3s_decode_rows, m3s_prefill_rows,
+Functions carry the C names: m3s_store, m3s_decode_rows, m3s_store_and_rows, m3s_prefill_rows,
 m3s_index_topk, m3s_sparse_attend, m3s_workspace_bytes, m3s_read_device_status,
 m3s_status_string, m3s_version.
 """
@@ -32,7 +32,8 @@ DEV_BITS = {
     "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6,
 }
 
-EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_prefill_rows", "m3s_index_topk", "m3s_sparse_attend",
+EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_index_topk",
+           "m3s_sparse_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
 MAX_GROUPS = 4096
 GROUP_ROWS = 16
@@ -76,6 +77,7 @@ def load(path: str | None = None):
         "m3s_store": (I32, [V, V, V, V, I64, V, I32, V, V]),
         "m3s_decode_rows": (I32, [V, V, I32, I32, V, V, V, V, V]),
         "m3s_prefill_rows": (I32, [V, V, I32, I32, I32, V, V, V, V, V, V, V]),
+        "m3s_store_and_rows": (I32, [V, V, V, V, I64, V, I32, V, V, I32, I32, V, V, V, V, V]),
         "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, I32, I32, V, V, SZ, V, V]),
         "m3s_sparse_attend": (I32, [V, V, I64, I64, I32, V, I32, I32, V, V, I32, F32, V, V, SZ, V, V]),
         "m3s_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
@@ -213,6 +215,33 @@ def m3s_decode_rows(cu_q, seq_lens, num_rows: int, row_req=None, row_len=None, r
     st = load().m3s_decode_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, _ptr(row_req), _ptr(row_len),
                                 _ptr(req_blk), _ptr(dev_status), _stream(stream))
     _check("m3s_decode_rows", st)
+    return Rows(cu_q, None, req_blk, row_req, row_len, B, num_rows)
+
+
+def m3s_store_and_rows(cache: Cache, k, v, idx, slot_mapping, cu_q, seq_lens, num_rows: int, row_req, row_len,
+                       req_blk, dev_status=None, stream=None):
+    """m3s_store and m3s_decode_rows in one launch (outputs written in place)."""
+    torch = _torch()
+    ref = next(t for t in (k, v, idx) if t is not None)
+    T = ref.shape[0]
+    stride = ref.stride(0)
+    for name, t in (("k", k), ("v", v), ("idx", idx)):
+        if t is not None:
+            _need(t, name, torch.bfloat16)
+            if t.shape[0] != T or t.stride(0) != stride or t.stride(1) != 1 or t.shape[1] < HEAD_DIM:
+                raise ValueError(f"{name}: rows must share [T, >=128] shape and row stride")
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    _need(cu_q, "cu_q", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    B = seq_lens.numel()
+    if slot_mapping.numel() != T or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 [T]")
+    if cu_q.numel() != B + 1:
+        raise ValueError("cu_q must have num_reqs + 1 entries")
+    st = load().m3s_store_and_rows(cache.ref(), _ptr(k), _ptr(v), _ptr(idx), stride, _ptr(slot_mapping), T,
+                                   _ptr(cu_q), _ptr(seq_lens), B, num_rows, _ptr(row_req), _ptr(row_len),
+                                   _ptr(req_blk), _ptr(dev_status), _stream(stream))
+    _check("m3s_store_and_rows", st)
     return Rows(cu_q, None, req_blk, row_req, row_len, B, num_rows)
 
 

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libm3s.so")
 
 HIP_SOURCES = ["store.hip", "rows.hip", "index_topk.hip", "attend.hip"]
 HOST_SOURCES = ["api.cpp"]
-HEADERS = ["fp4.hpp", "launch.hpp"]
+HEADERS = ["fp4.hpp", "launch.hpp", "rows_body.hpp"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]

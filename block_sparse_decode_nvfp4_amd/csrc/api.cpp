@@ -87,23 +87,25 @@ size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32
   return 0;
 }
 
-m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* v, const uint16_t* idx_k,
-                     int64_t row_stride, const int32_t* slot_mapping, int32_t num_tokens, uint32_t* dev_status,
-                     hipStream_t stream) {
+namespace {
+
+m3s_status store_args(StoreArgs& a, const m3s_cache* cache, const uint16_t* k, const uint16_t* v,
+                      const uint16_t* idx_k, int64_t row_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                      uint32_t* dev_status) {
   m3s_status st = check_cache(cache);
   if (st != M3S_OK) return st;
   if (num_tokens < 0) return M3S_ERR_INVALID_ARG;
-  if (num_tokens == 0) return M3S_OK;
-  if (!slot_mapping) return M3S_ERR_INVALID_ARG;
-  if (row_stride < M3S_HEAD_DIM || (row_stride & 7)) return M3S_ERR_INVALID_ARG;
-  const uint16_t* src[3] = {k, v, idx_k};
-  uint8_t* dat[3] = {cache->k_data, cache->v_data, cache->idx_data};
-  uint8_t* scl[3] = {cache->k_scale, cache->v_scale, cache->idx_scale};
-  for (int t = 0; t < 3; ++t) {
-    if (!src[t]) continue;
-    if (!aligned16(src[t]) || !dat[t] || !scl[t]) return M3S_ERR_INVALID_ARG;
+  if (num_tokens > 0) {
+    if (!slot_mapping) return M3S_ERR_INVALID_ARG;
+    if (row_stride < M3S_HEAD_DIM || (row_stride & 7)) return M3S_ERR_INVALID_ARG;
+    const uint16_t* src[3] = {k, v, idx_k};
+    uint8_t* dat[3] = {cache->k_data, cache->v_data, cache->idx_data};
+    uint8_t* scl[3] = {cache->k_scale, cache->v_scale, cache->idx_scale};
+    for (int t = 0; t < 3; ++t) {
+      if (!src[t]) continue;
+      if (!aligned16(src[t]) || !dat[t] || !scl[t]) return M3S_ERR_INVALID_ARG;
+    }
   }
-  StoreArgs a;
   a.format = cache->format;
   a.k = k;
   a.v = v;
@@ -119,18 +121,16 @@ m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* 
   a.idx_data = cache->idx_data;
   a.idx_scale = cache->idx_scale;
   a.status = dev_status;
-  return from_hip(launch_store(a, stream));
+  return M3S_OK;
 }
 
-m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
-                           int32_t* row_req, int32_t* row_len, int32_t* req_blk, uint32_t* dev_status,
-                           hipStream_t stream) {
+m3s_status rows_args(RowsArgs& a, const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs,
+                     int32_t num_rows, int32_t* row_req, int32_t* row_len, int32_t* req_blk, uint32_t* dev_status) {
   if (num_reqs < 0 || num_rows < 0) return M3S_ERR_INVALID_ARG;
   if (num_reqs > M3S_MAX_REQS || num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
   if (!cu_q || !req_blk) return M3S_ERR_INVALID_ARG;
   if (num_reqs > 0 && !seq_lens) return M3S_ERR_INVALID_ARG;
   if (num_rows > 0 && (!row_req || !row_len)) return M3S_ERR_INVALID_ARG;
-  RowsArgs a;
   a.cu_q = cu_q;
   a.seq_lens = seq_lens;
   a.num_reqs = num_reqs;
@@ -142,7 +142,41 @@ m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t
   a.grp_req = nullptr;
   a.max_groups = 0;
   a.status = dev_status;
+  return M3S_OK;
+}
+
+}  // namespace
+
+m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* v, const uint16_t* idx_k,
+                     int64_t row_stride, const int32_t* slot_mapping, int32_t num_tokens, uint32_t* dev_status,
+                     hipStream_t stream) {
+  StoreArgs a;
+  const m3s_status st = store_args(a, cache, k, v, idx_k, row_stride, slot_mapping, num_tokens, dev_status);
+  if (st != M3S_OK || num_tokens == 0) return st;
+  return from_hip(launch_store(a, stream));
+}
+
+m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
+                           int32_t* row_req, int32_t* row_len, int32_t* req_blk, uint32_t* dev_status,
+                           hipStream_t stream) {
+  RowsArgs a;
+  const m3s_status st = rows_args(a, cu_q, seq_lens, num_reqs, num_rows, row_req, row_len, req_blk, dev_status);
+  if (st != M3S_OK) return st;
   return from_hip(launch_decode_rows(a, stream));
+}
+
+m3s_status m3s_store_and_rows(const m3s_cache* cache, const uint16_t* k, const uint16_t* v, const uint16_t* idx_k,
+                              int64_t row_stride, const int32_t* slot_mapping, int32_t num_tokens,
+                              const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
+                              int32_t* row_req, int32_t* row_len, int32_t* req_blk, uint32_t* dev_status,
+                              hipStream_t stream) {
+  StoreArgs s;
+  m3s_status st = store_args(s, cache, k, v, idx_k, row_stride, slot_mapping, num_tokens, dev_status);
+  if (st != M3S_OK) return st;
+  RowsArgs r;
+  st = rows_args(r, cu_q, seq_lens, num_reqs, num_rows, row_req, row_len, req_blk, dev_status);
+  if (st != M3S_OK) return st;
+  return from_hip(launch_store_rows(s, r, stream));
 }
 
 m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,

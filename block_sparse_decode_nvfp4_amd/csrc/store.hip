@@ -21,6 +21,7 @@
 // rr = token * 3 + tensor so a token's three rows sit in one workgroup.
 #include "fp4.hpp"
 #include "launch.hpp"
+#include "rows_body.hpp"
 
 namespace m3s {
 
@@ -73,9 +74,9 @@ __device__ __forceinline__ uint32_t e2m1_mag(float a, float s) {
 __device__ __forceinline__ uint32_t neg(uint32_t bits) { return (bits >> 15) & ((bits & 0x7FFFu) != 0u); }
 
 template <int FMT>
-__global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
+__device__ __forceinline__ void store_body(const StoreArgs& a, int64_t block) {
   const int lane16 = threadIdx.x & 15;
-  const int64_t rr = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t rr = block * 16 + (threadIdx.x >> 4);
   const int64_t tok = rr / 3;
   const int ten = (int)(rr - tok * 3);
   const uint16_t* src = ten == 0 ? a.k : (ten == 1 ? a.v : a.idx);
@@ -137,6 +138,21 @@ __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {
+  store_body<FMT>(a, blockIdx.x);
+}
+
+// Store and decode row map in one launch: workgroups [0, store_grid) store, the
+// last one builds the row map (the two are independent; one launch instead of
+// two, each of which is mostly launch and first-load latency).
+template <int FMT>
+__global__ __launch_bounds__(256) void store_rows_kernel(StoreArgs s, RowsArgs r, int store_grid) {
+  __shared__ int s_scan[256 / 64];
+  if ((int)blockIdx.x < store_grid) store_body<FMT>(s, blockIdx.x);
+  else decode_rows_body<256>(r, s_scan);
+}
+
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * 3;
   const int64_t grid = (rows + 15) / 16;
@@ -145,6 +161,15 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(store_kernel<1>, dim3((unsigned)grid), dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(store_kernel<2>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t stream) {
+  const int64_t grid = ((int64_t)s.num_tokens * 3 + 15) / 16;
+  if (s.format == 1)
+    hipLaunchKernelGGL(store_rows_kernel<1>, dim3((unsigned)grid + 1), dim3(256), 0, stream, s, r, (int)grid);
+  else
+    hipLaunchKernelGGL(store_rows_kernel<2>, dim3((unsigned)grid + 1), dim3(256), 0, stream, s, r, (int)grid);
   return hipGetLastError();
 }
 

@@ -191,6 +191,20 @@ m3s_status m3s_decode_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t
                            int32_t* req_blk, uint32_t* dev_status, hipStream_t stream);
 
 /*
+ * m3s_store_and_rows - m3s_store and m3s_decode_rows in one launch (the two
+ * are independent: the store writes the planes, the row map its own arrays).
+ * Arguments, validation, results and status bits are those of the two calls;
+ * a call that would fail either of them launches nothing. For a caller that
+ * runs both each step, it saves one launch ([ATOM-2744] Design, Write path:
+ * the pages measure the store as launch-bound).
+ */
+m3s_status m3s_store_and_rows(const m3s_cache* cache, const uint16_t* k, const uint16_t* v,
+                              const uint16_t* idx_k, int64_t row_stride, const int32_t* slot_mapping,
+                              int32_t num_tokens, const int32_t* cu_q, const int32_t* seq_lens,
+                              int32_t num_reqs, int32_t num_rows, int32_t* row_req, int32_t* row_len,
+                              int32_t* req_blk, uint32_t* dev_status, hipStream_t stream);
+
+/*
  * m3s_prefill_rows - [ATOM-2744] Design, row maps (prefill_rows): every query
  * token of a request's prefill chunk is a row; row r of request b sees
  *   row_len = seq_lens[b] - (cu_q[b+1] - cu_q[b]) + 1 + (r - cu_q[b])

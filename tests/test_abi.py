@@ -180,3 +180,18 @@ def test_prefill_rows_validation(lib):
     assert f(gb=None) == E.ERR_INVALID_ARG
     assert f(rr=None) == E.ERR_INVALID_ARG
 
+
+
+def test_store_and_rows_validation(lib):
+    E = m3s
+    f = lambda cache=None, k=FAKE, stride=128, slots=FAKE, T=1, cu=FAKE, seq=FAKE, B=1, R=1, rb=FAKE: \
+        lib.m3s_store_and_rows(ctypes.byref(_cache() if cache is None else cache), k, None, None, stride, slots, T,
+                               cu, seq, B, R, FAKE, FAKE, rb, None, None)
+    assert f(T=-1) == E.ERR_INVALID_ARG
+    assert f(slots=None) == E.ERR_INVALID_ARG
+    assert f(stride=100) == E.ERR_INVALID_ARG
+    assert f(cache=_cache(page=64)) == E.ERR_UNSUPPORTED
+    assert f(B=-1) == E.ERR_INVALID_ARG
+    assert f(B=5000) == E.ERR_UNSUPPORTED
+    assert f(cu=None) == E.ERR_INVALID_ARG
+    assert f(rb=None) == E.ERR_INVALID_ARG

@@ -114,3 +114,39 @@ def test_prefill_rows_reject(gpu):
         rr, rl, gr, gq, gb, st = _prefill(gpu, cu, seq, R, G)
         assert st & bad_bit
         assert np.all(rr == -1) and np.all(rl == 0) and gb[-1] == 0 and np.all(gq == -1)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_store_and_rows_equals_separate_calls(gpu, fmt):
+    """One launch for store + row map writes what the two separate calls write, status
+    bits included (a slot past the cache and a rejected request)."""
+    rng = np.random.default_rng(12)
+    T, P = 300, 8
+    g = torch.Generator(device="cpu").manual_seed(3)
+    x = (torch.randn((3, T, 128), generator=g) * 3).to(torch.bfloat16).to(DEV)
+    slots = torch.as_tensor(rng.permutation(P * 128)[:T].astype(np.int32), device=DEV)
+    slots[7] = P * 128 + 5   # bad slot
+    slots[9] = -1            # pad row
+    ql = rng.integers(1, 17, size=40)
+    ql[3] = 20               # rejected request
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(ql)]).astype(np.int32), device=DEV)
+    seq = torch.as_tensor((ql + rng.integers(0, 9000, size=40)).astype(np.int32), device=DEV)
+    R = int(cu[-1].item()) + 5
+    outs = []
+    for fused in (False, True):
+        c = gpu.Cache(fmt, P, DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        rr = torch.full((R,), 77, dtype=torch.int32, device=DEV)
+        rl = torch.full((R,), 77, dtype=torch.int32, device=DEV)
+        rb = torch.full((41,), 77, dtype=torch.int32, device=DEV)
+        if fused:
+            gpu.m3s_store_and_rows(c, x[0], x[1], x[2], slots, cu, seq, R, rr, rl, rb, st)
+        else:
+            gpu.m3s_store(c, x[0], x[1], x[2], slots, st)
+            gpu.m3s_decode_rows(cu, seq, R, rr, rl, rb, st)
+        torch.cuda.synchronize()
+        outs.append(([t.cpu() for pl in c.planes.values() for t in pl], rr.cpu(), rl.cpu(), rb.cpu(), int(st.item())))
+    (pa, ra, la, ba, sa), (pb, rb_, lb, bb, sb) = outs
+    assert all(torch.equal(u, w) for u, w in zip(pa, pb))
+    assert torch.equal(ra, rb_) and torch.equal(la, lb) and torch.equal(ba, bb)
+    assert sa == sb and sa & gpu.DEV_BITS["BAD_SLOT"] and sa & gpu.DEV_BITS["BAD_ROWS"]
