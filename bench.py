@@ -32,11 +32,43 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(text):
+    """C++ source without comments, trailing blanks or empty lines (what the compiler sees
+    of the kernels, so that a comment edit does not invalidate a counter record)."""
+    out, i, n, quote = [], 0, len(text), None
+    while i < n:
+        c = text[i]
+        if quote:
+            out.append(c)
+            if c == "\\" and i + 1 < n:
+                out.append(text[i + 1])
+                i += 1
+            elif c == quote:
+                quote = None
+        elif c in "\"'":
+            quote = c
+            out.append(c)
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+            continue
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+            continue
+        else:
+            out.append(c)
+        i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def source_sha(paths):
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -18,11 +18,12 @@
 //            with fp16 MFMA (K tile as A, queries as B, fp32 accumulate) and
 //            writes, per row, the block's fp32 score and a rigorous bound on
 //            its error.
-//   select - one workgroup per row: radix-select the top-k of the fp32 scores
-//            by (score, id), then certify: a block whose rank the error bound
-//            leaves open is rescored in exact float64 and the open slots are
-//            filled from those exact scores. The result is the selection that
-//            exact arithmetic makes.
+//   select - one workgroup per row: the k-th and (k+1)-th best fp32 scores by
+//            (score, id), from a threshold on per-wave sorted maxima and one
+//            sort of the keys above it; then certify: a block whose rank the
+//            error bound leaves open is rescored in exact float64 and the open
+//            slots are filled from those exact scores. The result is the
+//            selection that exact arithmetic makes.
 //
 // Error bound of the scan (per row and block). The query row is scaled by a
 // power of two 2^P (exact) and rounded to fp16 (error e_d, computed exactly);
@@ -450,9 +451,9 @@ __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) { return bitonic_
 //      one wave as (score, tie-rule id), giving the k-th and (k+1)-th keys
 //      exactly; an iterative extraction covers larger sets and k = 64;
 //   2. certification against the row's error bound, in one pass: blocks above
-//      hi are in, below lo out, the band between is listed (with its pages,
-//      whose loads start at once) and rescored in exact float64 by all threads
-//      when it does not exactly fill the open slots;
+//      hi are in, below lo out, the band between is listed with its pages; when
+//      it does not exactly fill the open slots each band block is rescored in
+//      exact float64 by one wave, over only the tokens its bound leaves open;
 //   3. the k selected ids are gathered in LDS and one wave sorts them ascending.
 // Score registers per thread: PER = 8, 16 or 32 (rows of up to 256 PER blocks),
 // picked at launch from max_blocks; the smallest that fits keeps the kernel's
