@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode rows/s + achieved HBM GB/s (store+score+top-k+attend), 8 req x 8 rows @150K"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}  # dense, MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_topk_b8x8_150k_traffic.json")
 INDEX_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/index_topk.hip", "block_sparse_decode_nvfp4_amd/csrc/fp4.hpp"]
 
@@ -70,6 +71,14 @@ def source_sha(paths):
         with open(os.path.join(ROOT, p), encoding="utf-8") as f:
             h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
+
+
+def row_lens_of(lay):
+    """Causal length of every row: row i of a request with q_len rows sees
+    seq_len - q_len + 1 + i tokens."""
+    import numpy as np
+    return np.concatenate([np.arange(int(s) - int(q) + 1, int(s) + 1, dtype=np.int64)
+                           for s, q in zip(lay.seq_lens, lay.q_lens)])
 
 
 def step_bytes(cfg, lay, ids_np, G):
@@ -410,6 +419,18 @@ def main():
                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "m3s_index_topk (index_scan + index_select kernels)",
                     "launch_us": round(stage_ms[1] * 1e3, 2), "bytes_per_launch": by["index_call"]}
+        if prefill:
+            # A prefill chunk's pages stay in the caches while every 16-row group re-scores
+            # them: the scan is bound by the matrix cores, not HBM. Algorithmic work is one
+            # 128-dim dot product (256 flop) per (row, causal token); the NVFP4 scan runs on
+            # fp16 MFMA, the MXFP4 scan on the scaled fp4 x fp8 MFMA (fp8 rate).
+            flop = 256 * int(row_lens_of(lay).astype("int64").sum())
+            peak = MFMA_PEAK_TFLOPS["f16" if cfg.fmt == "nvfp4" else "fp8"]
+            tf_s = flop / t_idx / 1e12
+            roofline = {"bound": "mfma", "achieved": round(tf_s, 1), "peak": peak, "unit": "TFLOP/s",
+                        "frac": round(tf_s / peak, 4), "traffic": None,
+                        "kernel": "m3s_index_topk (index_scan + index_select kernels)",
+                        "launch_us": round(stage_ms[1] * 1e3, 2), "flop_per_launch": flop}
 
     cpu = None
     if not args.no_cpu and not prefill:  # the oracle on a 4096-row chunk takes hours
