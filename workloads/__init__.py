@@ -224,3 +224,47 @@ def bf16_bits(t) -> np.ndarray:
     """uint16 numpy view of a torch bfloat16 tensor (copied to host)."""
     torch = _torch()
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# inputs of the fused producer store (pre-norm rows, norm weights, angle table)
+# ---------------------------------------------------------------------------
+
+def gen_norm_weights(seed: int, device="cpu"):
+    """bf16 [4, 128] RMS-norm weights (query, key, index query, index key):
+    1 + 0.1 N(0, 1), rounded to bf16."""
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 100 + 80)
+    w = 1.0 + 0.1 * torch.randn((4, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    return w.to(torch.bfloat16)
+
+
+def gen_prenorm_rows(shape, seed: int, which: int, device="cpu"):
+    """bf16 pre-norm rows [..., 128]: N(0, 1) times a per-row scale drawn
+    log-uniformly from [1/4, 16], with the tensor family's 3 outlier channels x8."""
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 100 + 60 + int(which))
+    shape = tuple(shape)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    ch = torch.as_tensor(outlier_channels(seed, 10 + which), device=device)
+    x[..., ch] *= 8.0
+    u = torch.rand(shape[:-1] + (1,), generator=g, device=device, dtype=torch.float32)
+    x = x * torch.exp2(u * 6.0 - 2.0)
+    return x.to(torch.bfloat16)
+
+
+def rope_table(max_pos: int, rotary_dim: int, base: float = 10000.0) -> np.ndarray:
+    """float32 [max_pos, rotary_dim]: cos(p * t_d) in columns [0, rd/2) and
+    sin(p * t_d) in [rd/2, rd), t_d = base^(-2d / rd), computed in float64 and
+    rounded to float32 (an input of the producer, like its weights)."""
+    h = rotary_dim // 2
+    if h == 0:
+        return np.zeros((max_pos, 0), dtype=np.float32)
+    t = base ** (-2.0 * np.arange(h, dtype=np.float64) / rotary_dim)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * t[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+PQ_FAMILY, PK_FAMILY, PV_FAMILY, PIQ_FAMILY, PIK_FAMILY = 0, 1, 2, 3, 4
