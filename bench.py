@@ -24,6 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode rows/s + achieved HBM GB/s (store+score+top-k+attend), 8 req x 8 rows @150K"
 HBM_PEAK_GBS = 8000.0
+PRODUCER_ROTARY_DIM = 64   # rotary dims of the producer measurement (half the head)
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}  # dense, MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_topk_b8x8_150k_traffic.json")
 INDEX_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/index_topk.hip", "block_sparse_decode_nvfp4_amd/csrc/fp4.hpp"]
@@ -374,6 +375,25 @@ def main():
                                                            ids, ws_i, status)),
               ("sparse_attend", lambda c: m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids,
                                                                  cfg.sm_scale, out, ws_a, status))]
+    if not prefill:
+        # the fused producer store (norm + rotary + FP4 store + query rows) for the step's new
+        # tokens, beside the plain store of the same rows, each into its own one-page cache
+        # (the layer caches keep the bytes the step stored)
+        T_new = int(new_idx.numel())
+        pc = m3s.Cache(cfg.fmt, (T_new + 127) // 128, dev)
+        p_slots = torch.arange(T_new, dtype=torch.int32, device=dev)
+        p_q = W.gen_prenorm_rows((T_new, G, 128), cfg.seed, W.PQ_FAMILY, dev)
+        p_rows = [W.gen_prenorm_rows((T_new, 128), cfg.seed, f, dev)
+                  for f in (W.PK_FAMILY, W.PV_FAMILY, W.PIQ_FAMILY, W.PIK_FAMILY)]
+        p_w = W.gen_norm_weights(cfg.seed, dev)
+        p_cs = torch.as_tensor(W.rope_table(int(lay.seq_lens.max()), PRODUCER_ROTARY_DIM), device=dev)
+        p_pos = torch.as_tensor(W.new_positions(lay), device=dev)
+        p_out = (torch.empty((T_new, G, 128), dtype=torch.bfloat16, device=dev),
+                 torch.empty((T_new, 128), dtype=torch.bfloat16, device=dev))
+        stages += [("qknorm_rope_store", lambda c: m3s.m3s_qknorm_rope_store(
+                       pc, p_q, *p_rows, p_w, 1e-6, p_pos, p_cs, p_slots, q_out=p_out[0], idx_q_out=p_out[1],
+                       dev_status=status)),
+                   ("store", lambda c: m3s.m3s_store(pc, k_new, v_new, i_new, p_slots, status))]
     reps = max(1, args.stage_reps)
     stage_ms = []
     for _, fn in stages:

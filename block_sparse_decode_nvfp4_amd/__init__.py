@@ -7,8 +7,8 @@ the path runs in the library's HIP kernels. Loading fails loudly when the
 library is missing: there is no fallback.
 
 Functions carry the C names: m3s_store, m3s_decode_rows, m3s_store_and_rows, m3s_prefill_rows,
-m3s_index_topk, m3s_sparse_attend, m3s_workspace_bytes, m3s_read_device_status,
-m3s_status_string, m3s_version.
+m3s_qknorm_rope_store, m3s_index_topk, m3s_sparse_attend, m3s_workspace_bytes,
+m3s_read_device_status, m3s_status_string, m3s_version.
 """
 from __future__ import annotations
 
@@ -29,11 +29,11 @@ OP_INDEX_TOPK, OP_SPARSE_ATTEND = 1, 2
 TOPK_TIE_HIGH_ID = 1
 DEV_BITS = {
     "BAD_SLOT": 1 << 0, "BAD_ROWS": 1 << 1, "BAD_LENGTH": 1 << 2, "BAD_PAGE": 1 << 3,
-    "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6,
+    "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6, "BAD_POSITION": 1 << 7,
 }
 
-EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_index_topk",
-           "m3s_sparse_attend",
+EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_qknorm_rope_store",
+           "m3s_index_topk", "m3s_sparse_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
 MAX_GROUPS = 4096
 GROUP_ROWS = 16
@@ -78,6 +78,8 @@ def load(path: str | None = None):
         "m3s_decode_rows": (I32, [V, V, I32, I32, V, V, V, V, V]),
         "m3s_prefill_rows": (I32, [V, V, I32, I32, I32, V, V, V, V, V, V, V]),
         "m3s_store_and_rows": (I32, [V, V, V, V, I64, V, I32, V, V, I32, I32, V, V, V, V, V]),
+        "m3s_qknorm_rope_store": (I32, [V, V, I64, I32, V, V, V, V, I64, V, F32, V, V, I32, I32, V, I32,
+                                        V, V, V, V, V]),
         "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, I32, I32, V, V, SZ, V, V]),
         "m3s_sparse_attend": (I32, [V, V, I64, I64, I32, V, I32, I32, V, V, I32, F32, V, V, SZ, V, V]),
         "m3s_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
@@ -198,6 +200,50 @@ def m3s_store(cache: Cache, k, v, idx, slot_mapping, dev_status=None, stream=Non
     st = load().m3s_store(cache.ref(), _ptr(k), _ptr(v), _ptr(idx), stride, _ptr(slot_mapping), T,
                           _ptr(dev_status), _stream(stream))
     _check("m3s_store", st)
+
+
+def m3s_qknorm_rope_store(cache: Cache, q, k, v, idx_q, idx_k, norm_weights, eps: float, positions, cos_sin,
+                          slot_mapping, q_out=None, idx_q_out=None, q_out_e4m3=None, want_e4m3: bool = False,
+                          dev_status=None, stream=None):
+    """The fused producer store: RMS norm + rotary of q [T, G, >=128 per head] / k / idx_q / idx_k,
+    FP4 store of k, v, idx_k at slot_mapping, query rows out. cos_sin is float32 [max_pos, rotary_dim]
+    (rotary_dim = cos_sin.shape[1], 0 for none). Returns (q_out, idx_q_out, q_out_e4m3 or None)."""
+    torch = _torch()
+    _need(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or q.stride(2) != 1 or q.stride(1) != HEAD_DIM:
+        raise ValueError("q must be [T, G, 128] with heads 128 elements apart")
+    T, G = q.shape[0], q.shape[1]
+    stride = k.stride(0)
+    for name, t in (("k", k), ("v", v), ("idx_q", idx_q), ("idx_k", idx_k)):
+        _need(t, name, torch.bfloat16)
+        if t.shape[0] != T or t.stride(0) != stride or t.stride(1) != 1 or t.shape[1] < HEAD_DIM:
+            raise ValueError(f"{name}: rows must share [T, >=128] shape and row stride")
+    _need(norm_weights, "norm_weights", torch.bfloat16)
+    if tuple(norm_weights.shape) != (4, HEAD_DIM) or not norm_weights.is_contiguous():
+        raise ValueError("norm_weights must be a contiguous bf16 [4, 128]")
+    _need(cos_sin, "cos_sin", torch.float32)
+    if cos_sin.dim() != 2 or not cos_sin.is_contiguous():
+        raise ValueError("cos_sin must be a contiguous float32 [max_pos, rotary_dim]")
+    rd = cos_sin.shape[1]
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    if slot_mapping.numel() != T or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 [T]")
+    if positions is not None:
+        _need(positions, "positions", torch.int32)
+        if positions.numel() != T or not positions.is_contiguous():
+            raise ValueError("positions must be a contiguous int32 [T]")
+    dev = q.device
+    q_out = torch.empty((T, G, HEAD_DIM), dtype=torch.bfloat16, device=dev) if q_out is None else q_out
+    idx_q_out = torch.empty((T, HEAD_DIM), dtype=torch.bfloat16, device=dev) if idx_q_out is None else idx_q_out
+    if q_out_e4m3 is None and want_e4m3:
+        q_out_e4m3 = torch.empty((T, G, HEAD_DIM), dtype=torch.uint8, device=dev)
+    st = load().m3s_qknorm_rope_store(cache.ref(), _ptr(q), q.stride(0), G, _ptr(k), _ptr(v), _ptr(idx_q),
+                                      _ptr(idx_k), stride, _ptr(norm_weights), float(eps), _ptr(positions),
+                                      _ptr(cos_sin) if rd > 0 else None, cos_sin.shape[0], rd,
+                                      _ptr(slot_mapping), T, _ptr(q_out), _ptr(q_out_e4m3), _ptr(idx_q_out),
+                                      _ptr(dev_status), _stream(stream))
+    _check("m3s_qknorm_rope_store", st)
+    return q_out, idx_q_out, q_out_e4m3
 
 
 def m3s_decode_rows(cu_q, seq_lens, num_rows: int, row_req=None, row_len=None, req_blk=None,

@@ -179,6 +179,66 @@ m3s_status m3s_store_and_rows(const m3s_cache* cache, const uint16_t* k, const u
   return from_hip(launch_store_rows(s, r, stream));
 }
 
+m3s_status m3s_qknorm_rope_store(const m3s_cache* cache, const uint16_t* q, int64_t q_stride,
+                                 int32_t num_heads, const uint16_t* k, const uint16_t* v,
+                                 const uint16_t* idx_q, const uint16_t* idx_k, int64_t row_stride,
+                                 const uint16_t* norm_weights, float eps, const int32_t* positions,
+                                 const float* cos_sin, int32_t max_pos, int32_t rotary_dim,
+                                 const int32_t* slot_mapping, int32_t num_tokens, uint16_t* q_out,
+                                 uint8_t* q_out_e4m3, uint16_t* idx_q_out, uint32_t* dev_status,
+                                 hipStream_t stream) {
+  m3s_status st = check_cache(cache);
+  if (st != M3S_OK) return st;
+  if (num_tokens < 0) return M3S_ERR_INVALID_ARG;
+  if (num_heads < 1 || num_heads > M3S_MAX_HEADS) return M3S_ERR_UNSUPPORTED;
+  if (rotary_dim < 0 || rotary_dim > M3S_HEAD_DIM || (rotary_dim & 15)) return M3S_ERR_UNSUPPORTED;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return M3S_ERR_INVALID_ARG;
+  if (num_tokens > 0) {
+    const void* in16[] = {q, k, v, idx_q, idx_k, norm_weights, q_out, idx_q_out};
+    for (const void* p : in16)
+      if (!p || !aligned16(p)) return M3S_ERR_INVALID_ARG;
+    if (!slot_mapping) return M3S_ERR_INVALID_ARG;
+    if (q_out_e4m3 && ((uintptr_t)q_out_e4m3 & 7u)) return M3S_ERR_INVALID_ARG;
+    if (q_stride < (int64_t)M3S_HEAD_DIM * num_heads || (q_stride & 7)) return M3S_ERR_INVALID_ARG;
+    if (row_stride < M3S_HEAD_DIM || (row_stride & 7)) return M3S_ERR_INVALID_ARG;
+    if (rotary_dim > 0 && (!positions || !cos_sin || !aligned16(cos_sin) || max_pos < 1)) return M3S_ERR_INVALID_ARG;
+    if (!cache->k_data || !cache->k_scale || !cache->v_data || !cache->v_scale || !cache->idx_data ||
+        !cache->idx_scale)
+      return M3S_ERR_INVALID_ARG;
+  }
+  if (num_tokens == 0) return M3S_OK;
+  ProducerArgs a;
+  a.format = cache->format;
+  a.q = q;
+  a.q_stride = q_stride;
+  a.num_heads = num_heads;
+  a.k = k;
+  a.v = v;
+  a.idx_q = idx_q;
+  a.idx_k = idx_k;
+  a.row_stride = row_stride;
+  a.norm_w = norm_weights;
+  a.eps = eps;
+  a.positions = positions;
+  a.cos_sin = cos_sin;
+  a.max_pos = rotary_dim > 0 ? max_pos : 0;
+  a.rotary_dim = rotary_dim;
+  a.slots = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_pages = cache->num_pages;
+  a.k_data = cache->k_data;
+  a.k_scale = cache->k_scale;
+  a.v_data = cache->v_data;
+  a.v_scale = cache->v_scale;
+  a.idx_data = cache->idx_data;
+  a.idx_scale = cache->idx_scale;
+  a.q_out = q_out;
+  a.q_out_e4m3 = q_out_e4m3;
+  a.idx_q_out = idx_q_out;
+  a.status = dev_status;
+  return from_hip(launch_producer(a, stream));
+}
+
 m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
                             int32_t max_groups, int32_t* row_req, int32_t* row_len, int32_t* grp_row,
                             int32_t* grp_req, int32_t* grp_blk, uint32_t* dev_status, hipStream_t stream) {

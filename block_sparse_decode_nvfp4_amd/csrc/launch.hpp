@@ -17,6 +17,7 @@ enum : uint32_t {
   kDevBadBlockId = 1u << 4,
   kDevInexact = 1u << 5,
   kDevBandOverflow = 1u << 6,
+  kDevBadPosition = 1u << 7,
 };
 
 constexpr int kMaxBlocks = 8192;   // causal blocks per request
@@ -38,6 +39,37 @@ struct StoreArgs {
   uint8_t* v_scale;
   uint8_t* idx_data;
   uint8_t* idx_scale;
+  uint32_t* status;
+};
+
+struct ProducerArgs {
+  int format;
+  const uint16_t* q;       // [T, q_stride], head h at h * 128
+  int64_t q_stride;
+  int32_t num_heads;
+  const uint16_t* k;       // k, v, idx_q, idx_k: [T, row_stride]
+  const uint16_t* v;
+  const uint16_t* idx_q;
+  const uint16_t* idx_k;
+  int64_t row_stride;
+  const uint16_t* norm_w;  // [4, 128]: query, key, index query, index key
+  float eps;
+  const int32_t* positions;
+  const float* cos_sin;    // [max_pos, rotary_dim]
+  int32_t max_pos;
+  int32_t rotary_dim;
+  const int32_t* slots;
+  int32_t num_tokens;
+  int32_t num_pages;
+  uint8_t* k_data;
+  uint8_t* k_scale;
+  uint8_t* v_data;
+  uint8_t* v_scale;
+  uint8_t* idx_data;
+  uint8_t* idx_scale;
+  uint16_t* q_out;         // [T, G, 128]
+  uint8_t* q_out_e4m3;     // [T, G, 128] or null
+  uint16_t* idx_q_out;     // [T, 128]
   uint32_t* status;
 };
 
@@ -114,6 +146,7 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows(const RowsArgs& a, hipStream_t stream);
 hipError_t launch_prefill_rows(const RowsArgs& a, hipStream_t stream);
 hipError_t launch_store_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t stream);
+hipError_t launch_producer(const ProducerArgs& a, hipStream_t stream);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);
 

@@ -97,9 +97,11 @@ enum {
   M3S_DEV_INEXACT = 1u << 5,      /* index_topk: an exact rescore could not prove its
                                      float64 sum exact (ids may then differ from exact
                                      arithmetic in a near tie) */
-  M3S_DEV_BAND_OVERFLOW = 1u << 6 /* index_topk: more than 1024 blocks inside a row's
-                                     uncertainty band; that row fell back to the
-                                     approximate scores */
+  M3S_DEV_BAND_OVERFLOW = 1u << 6, /* index_topk: more than 1024 blocks inside a row's
+                                      uncertainty band; that row fell back to the
+                                      approximate scores */
+  M3S_DEV_BAD_POSITION = 1u << 7   /* qknorm_rope_store: position outside [0, max_pos);
+                                      that token's outputs are left unwritten */
 };
 
 /* Flags of m3s_index_topk. */
@@ -203,6 +205,52 @@ m3s_status m3s_store_and_rows(const m3s_cache* cache, const uint16_t* k, const u
                               int32_t num_tokens, const int32_t* cu_q, const int32_t* seq_lens,
                               int32_t num_reqs, int32_t num_rows, int32_t* row_req, int32_t* row_len,
                               int32_t* req_blk, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * m3s_qknorm_rope_store - the fused producer store ([ATOM-2744] Follow-up:
+ * MXFP4 caches: the quantization moves into the fused qk-norm / RoPE / cache
+ * kernel, with no staging buffer and no store launch; [VLLM-64198] Claims: that
+ * kernel writes the K, V and index-K pages and the main query as e4m3). The
+ * pages do not define the norm or the rotary embedding; per token this call
+ * computes, in fp32, for each 128-dim row x of the G query heads, the key, the
+ * index query and the index key (weight rows 0, 1, 2, 3 of norm_weights):
+ *     y = x / sqrt(mean(x^2) + eps) * w
+ *     for d < h = rotary_dim / 2:  (y_d, y_{d+h}) <- (y_d c - y_{d+h} s, y_{d+h} c + y_d s)
+ *         c = cos_sin[pos][d], s = cos_sin[pos][h + d], pos = positions[t]
+ * and rounds each result to bf16 (to nearest even). The value row is neither
+ * normed nor rotated. Outputs:
+ *   q_out       bf16 [num_tokens, G, 128] (contiguous): the query rows;
+ *   q_out_e4m3  uint8 [num_tokens, G, 128] or NULL: E4M3FN bytes of q_out
+ *               (nearest, ties to even, saturating at 448, no scale);
+ *   idx_q_out   bf16 [num_tokens, 128] (contiguous): the index-query rows;
+ *   the cache   the key, value and index-key rows quantized at slot_mapping[t]
+ *               exactly as m3s_store quantizes these bf16 rows (pad tokens,
+ *               slot < 0, write no cache bytes but do write their queries).
+ * Inputs:
+ *   q           bf16 [num_tokens, q_stride], head h at elements [128 h, 128 h + 128);
+ *               q_stride >= 128 * num_heads, a multiple of 8
+ *   num_heads   G in [1, 16]
+ *   k, v, idx_q, idx_k  bf16 [num_tokens, row_stride] (first 128 used), row_stride >= 128,
+ *               a multiple of 8
+ *   norm_weights bf16 [4, 128]
+ *   eps         finite, >= 0
+ *   positions   int32 [num_tokens] (may be NULL when rotary_dim is 0)
+ *   cos_sin     float32 [max_pos, rotary_dim]: cos in columns [0, h), sin in [h, 2h)
+ *   rotary_dim  a multiple of 16 in [0, 128]
+ * Pointers to bf16, float and e4m3 data must be 16-byte aligned (q_out_e4m3:
+ * 8-byte). Errors: host validation returns M3S_ERR_INVALID_ARG /
+ * M3S_ERR_UNSUPPORTED without launching; a position outside [0, max_pos) sets
+ * M3S_DEV_BAD_POSITION and leaves that token's outputs unwritten; a slot >=
+ * num_pages * 128 sets M3S_DEV_BAD_SLOT and writes no cache bytes for it.
+ */
+m3s_status m3s_qknorm_rope_store(const m3s_cache* cache, const uint16_t* q, int64_t q_stride,
+                                 int32_t num_heads, const uint16_t* k, const uint16_t* v,
+                                 const uint16_t* idx_q, const uint16_t* idx_k, int64_t row_stride,
+                                 const uint16_t* norm_weights, float eps, const int32_t* positions,
+                                 const float* cos_sin, int32_t max_pos, int32_t rotary_dim,
+                                 const int32_t* slot_mapping, int32_t num_tokens, uint16_t* q_out,
+                                 uint8_t* q_out_e4m3, uint16_t* idx_q_out, uint32_t* dev_status,
+                                 hipStream_t stream);
 
 /*
  * m3s_prefill_rows - [ATOM-2744] Design, row maps (prefill_rows): every query

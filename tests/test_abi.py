@@ -195,3 +195,31 @@ def test_store_and_rows_validation(lib):
     assert f(B=5000) == E.ERR_UNSUPPORTED
     assert f(cu=None) == E.ERR_INVALID_ARG
     assert f(rb=None) == E.ERR_INVALID_ARG
+
+
+def test_qknorm_rope_store_validation(lib):
+    """Every call below fails host validation (or has no tokens) and launches nothing."""
+    MIS = ctypes.c_void_p(4096 + 8)      # 8-byte aligned only
+    I, U, A = m3s.ERR_INVALID_ARG, m3s.ERR_UNSUPPORTED, None
+
+    def f(cache=None, q=FAKE, qs=512, G=4, k=FAKE, v=FAKE, iq=FAKE, ik=FAKE, rs=128, w=FAKE, eps=1e-6,
+          pos=FAKE, cs=FAKE, mp=16, rd=64, sl=FAKE, T=3, qo=FAKE, qe=None, iqo=FAKE):
+        c = _cache() if cache is None else cache
+        return lib.m3s_qknorm_rope_store(ctypes.byref(c), q, qs, G, k, v, iq, ik, rs, w, eps, pos, cs, mp, rd,
+                                         sl, T, qo, qe, iqo, None, None)
+
+    assert f(T=0) == m3s.OK                                 # nothing to do: no launch
+    assert f(cache=_cache(fmt=3)) == U
+    assert f(cache=_cache(page=64)) == U
+    assert f(T=-1) == I
+    assert f(G=0) == U and f(G=17) == U
+    assert f(rd=40) == U and f(rd=144) == U and f(rd=-16) == U
+    assert f(eps=-1.0) == I and f(eps=float("nan")) == I and f(eps=float("inf")) == I
+    for name in ("q", "k", "v", "iq", "ik", "w", "qo", "iqo", "sl"):
+        assert f(**{name: None}) == I, name
+    for name in ("q", "k", "v", "iq", "ik", "w", "qo", "iqo", "cs"):
+        assert f(**{name: MIS}) == I, name
+    assert f(qe=ctypes.c_void_p(4096 + 4)) == I             # e4m3 output needs 8-byte alignment
+    assert f(qs=511) == I and f(G=4, qs=504) == I and f(rs=120) == I and f(rs=132) == I
+    assert f(pos=None) == I and f(cs=None) == I and f(mp=0) == I
+    assert f(cache=m3s.m3s_cache(1, 4, 128, 128, 1, 4096, 4096, None, 4096, 4096, 4096)) == I

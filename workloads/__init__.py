@@ -268,3 +268,12 @@ def rope_table(max_pos: int, rotary_dim: int, base: float = 10000.0) -> np.ndarr
 
 
 PQ_FAMILY, PK_FAMILY, PV_FAMILY, PIQ_FAMILY, PIK_FAMILY = 0, 1, 2, 3, 4
+
+
+def new_positions(layout: Layout) -> np.ndarray:
+    """int32 position (token index in its request) of every step row."""
+    out = []
+    for b in range(len(layout.seq_lens)):
+        s, q = int(layout.seq_lens[b]), int(layout.q_lens[b])
+        out.extend(range(s - q, s))
+    return np.asarray(out, dtype=np.int32)
