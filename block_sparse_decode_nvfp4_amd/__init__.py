@@ -36,7 +36,7 @@ EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_ro
            "m3s_index_topk", "m3s_sparse_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
 MAX_GROUPS = 4096
-GROUP_ROWS = 16
+GROUP_ROWS = 64
 
 _c_i32p = ctypes.c_void_p
 _lib = None
@@ -71,6 +71,9 @@ def load(path: str | None = None):
     if not os.path.exists(p):
         raise RuntimeError(f"{p} is missing: build it with __graft_entry__.build() "
                            "or python block_sparse_decode_nvfp4_amd/_build.py")
+    # torch first: the library then binds to the HIP runtime torch has loaded rather
+    # than loading a second copy beside it (two runtimes in one process fail launches)
+    _torch()
     lib = ctypes.CDLL(p)
     V, I32, I64, SZ, F32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     sig = {
@@ -166,7 +169,7 @@ class Cache:
 class Rows:
     """The row map of one step and the index scan's work groups (device tensors), with
     their m3s_rows struct. From m3s_decode_rows: one group per request (grp_row = cu_q,
-    grp_req None); from m3s_prefill_rows: 16-row groups."""
+    grp_req None); from m3s_prefill_rows: 64-row groups."""
 
     def __init__(self, grp_row, grp_req, grp_blk, row_req, row_len, num_groups: int, num_rows: int):
         self.grp_row, self.grp_req, self.grp_blk = grp_row, grp_req, grp_blk
@@ -293,8 +296,8 @@ def m3s_store_and_rows(cache: Cache, k, v, idx, slot_mapping, cu_q, seq_lens, nu
 
 def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = None, dev_status=None,
                      stream=None, out: Rows | None = None) -> Rows:
-    """Prefill row map and 16-row scan groups; max_groups defaults to the bound
-    ceil(num_rows / 16) + num_reqs (capped at MAX_GROUPS). ``out`` (a Rows from an
+    """Prefill row map and 64-row scan groups; max_groups defaults to the bound
+    ceil(num_rows / 64) + num_reqs (capped at MAX_GROUPS). ``out`` (a Rows from an
     earlier call with the same sizes) is written in place."""
     torch = _torch()
     _need(cu_q, "cu_q", torch.int32)

@@ -312,6 +312,7 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
   a.ws_bound = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
   a.status = dev_status;
   a.scan_grid = scan_grid();
+  a.group_tiles = rows->grp_req ? 4 : 1;
   return from_hip(launch_index_topk(a, stream));
 }
 

@@ -234,14 +234,55 @@ __device__ __forceinline__ void build_query(QueryTile& q, const IndexArgs& a, in
   }
 }
 
+// Query tile k of work group b: the group's rows 16 k .. 16 k + 15 (fewer at its end).
 template <int FMT>
-__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int n, int G) {
+__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int k, int n, int G) {
+  const int g0 = a.cu_q[b];
   q.b = b;
-  q.r0 = a.cu_q[b];
-  q.ql = a.cu_q[b + 1] - q.r0;
-  q.min_len = a.row_len[q.r0];
+  q.r0 = g0 + 16 * k;
+  q.ql = min(max(a.cu_q[b + 1] - q.r0, 0), 16);
+  q.min_len = q.ql > 0 ? a.row_len[q.r0] : 0x7FFFFFFF;
   q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
   build_query<FMT>(q, a, n < q.ql ? q.r0 + n : -1, n, G);
+}
+
+// S^T tile i of a page against NT query tiles: acc[k][v] = (scaled) score of
+// token 16 i + 4 G + v against the query in column n (lane (n, G)) of tile k.
+// The K tile is decoded once for all NT tiles, and each column's result is the
+// same as with that tile alone (columns of an MFMA do not interact). NVFP4 also
+// returns the tile's scales.
+template <int FMT, int NT>
+__device__ __forceinline__ void tile_scores_n(const PageBuf& p, const QueryTile (&q)[NT], int i, f16x2& sc,
+                                              f32x4 (&acc)[NT]) {
+#pragma unroll
+  for (int k = 0; k < NT; ++k) acc[k] = {0.f, 0.f, 0.f, 0.f};
+  // pin the tile's words here: keeps the compiler from decoding every tile of the
+  // page ahead of the MFMAs (each decoded tile holds 20+ registers)
+  u32x4 kw = p.kr[i];
+  uint32_t ksw = p.ks[i];
+  asm volatile("" : "+v"(kw), "+v"(ksw));
+  if (FMT == 1) {
+    // both E4M3 scales of the lane's two groups in one conversion (OCP E4M3FN, exact)
+    const auto sf = __builtin_amdgcn_cvt_pk_f32_fp8((int)ksw, false);
+    sc = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[1]));
+    const f16x8 s0 = {sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+    const f16x8 s1 = {sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f16x8 kd = fp4x8_to_f16_unscaled(kw[c]) * (c < 2 ? s0 : s1);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) acc[k] = mfma_f16(kd, q[k].op[c], acc[k]);
+    }
+  } else {
+    // the lane's 32 codes and E8M0 byte are the fp4 A operand and its scale as loaded
+    const i32x8 ka = {(int)kw[0], (int)kw[1], (int)kw[2], (int)kw[3], 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int k = 0; k < NT; ++k)
+        acc[k] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, q[k].qb[t], acc[k], 4, 0, 0, (int)ksw, 0,
+                                                                  q[k].qsc[t]);
+  }
 }
 
 // S^T tile i of a page: acc[v] = (scaled) score of token 16 i + 4 G + v against
@@ -309,19 +350,79 @@ __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q,
   }
 }
 
-// Streaming scan. The (request, block) units of all requests form one flat list
-// (block fastest). Workgroup g (16 waves, one per CU) takes the contiguous slice
+// Score one page against the work group's rows (NT query tiles); write each
+// row's fp32 score and error bound.
+template <int FMT, int NT>
+__device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (&q)[NT], const IndexArgs& a, int j,
+                                             int n, int G) {
+  bool need_mask[NT];
+  float run[NT];
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    need_mask[k] = (j + 1) * kPage > q[k].min_len;
+    run[k] = -INFINITY;
+  }
+  f16x2 smx = {(_Float16)0.f, (_Float16)0.f};  // largest scale of groups (2G, 2G+1) seen by this lane
+  float smx_mx = 0.f;                          // MXFP4: largest E8M0 scale of group G
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f16x2 sc;
+    f32x4 acc[NT];
+    tile_scores_n<FMT, NT>(p, q, i, sc, acc);
+    if (FMT == 1) smx = __builtin_elementwise_max(smx, sc);
+    else smx_mx = fmaxf(smx_mx, e8m0_to_f32(p.ks[i]));
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      if (need_mask[k]) {
+        const int t0 = j * kPage + 16 * i + 4 * G;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          if (t0 + v >= q[k].len_n) acc[k][v] = -INFINITY;
+      }
+      run[k] = __builtin_fmaxf(__builtin_fmaxf(run[k], acc[k][0]), acc[k][1]);
+      run[k] = __builtin_fmaxf(__builtin_fmaxf(run[k], acc[k][2]), acc[k][3]);
+      asm volatile("" : "+v"(run[k]));  // the tile is finished before the next one is decoded
+    }
+  }
+  float m0, m1 = 0.f;
+  if (FMT == 1) {
+    m0 = lane_fmax<1, 16>((float)smx[0]);
+    m1 = lane_fmax<1, 16>((float)smx[1]);
+  } else {
+    m0 = lane_fmax<1, 16>(smx_mx);
+  }
+#pragma unroll
+  for (int k = 0; k < NT; ++k) {
+    const float r = lane_fmax<16, 64>(run[k]);
+    float part = FMT == 1 ? 6.0f * (m0 * (kAccRel * q[k].qs0 + q[k].qe0) + m1 * (kAccRel * q[k].qs1 + q[k].qe1))
+                          : 6.0f * m0 * (kAccRel * q[k].qs0 + q[k].qe0);
+    part = lane_sum<16, 64>(part);
+    if (G == 0 && n < q[k].ql) {
+      const int64_t o = (int64_t)(q[k].r0 + n) * a.max_blocks + j;
+      a.ws_score[o] = r * q[k].unscale;
+      a.ws_bound[o] = part * q[k].unscale * (1.0f + 0x1p-10f);
+    }
+  }
+}
+
+// Streaming scan. The (work group, block) units of all groups form one flat list
+// (block fastest). Workgroup g (one per CU) takes the contiguous slice
 // [g * N / W, (g + 1) * N / W), so consecutive slices of a long request land on
 // different XCDs. The slice's block-table entries are staged in LDS, and its
 // waves claim units one at a time from an LDS counter: a wave whose pages arrive
 // late simply takes fewer units, so the waves of a workgroup finish together.
 // Each wave keeps one page in flight: measured, 16 waves with one page each beat
 // 8 waves with two or three (deeper per-wave prefetch only deepens the queue).
-constexpr int kScanWaves = 16;
+// Decode groups (one request, <= 16 rows) use NT = 1 query tile and 16 waves.
+// Prefill groups (<= 64 rows) use 8 waves, for the registers of more query
+// tiles: NVFP4 scores all 64 rows at once (NT = 4, so each decoded K tile feeds
+// four MFMA column tiles); MXFP4, whose query tiles take three e4m3 terms each,
+// scores them in H = 2 passes of NT = 2 tiles, a (group, block, half) unit each.
 constexpr int kScanChunk = 1024;  // units staged in LDS at a time
 
-template <int FMT>
-__global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a) {
+template <int FMT, int NT, int WAVES, int H>
+__global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
+  constexpr int kScanWaves = WAVES;
   __shared__ int s_blk[M3S_MAX_REQS_INTERNAL + 1];
   __shared__ int s_unit[kScanChunk];  // request * kMaxBlocks + block; -1: not scored
   __shared__ int s_page[kScanChunk];  // page; -1: unusable
@@ -331,7 +432,7 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a
   const int B = a.num_reqs;
   for (int i = tid; i <= B; i += kScanWaves * 64) s_blk[i] = a.req_blk[i];
   __syncthreads();
-  const int64_t total = s_blk[B];
+  const int64_t total = (int64_t)s_blk[B] * H;
   const int64_t w0 = (int64_t)blockIdx.x * total / gridDim.x;
   const int64_t w1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
 
@@ -349,32 +450,45 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a
     return __builtin_amdgcn_readlane(v, 0);
   };
 
-  QueryTile qt;
-  qt.b = -1;
+  QueryTile qt[NT];
+  int qb = -1;  // (work group, pass) whose query tiles qt holds
   PageBuf pa;
   auto process = [&](const PageBuf& buf, int i) {
     const int key = s_unit[i];
     if (key < 0) return;
-    const int bb = key / kMaxBlocks, j = key - bb * kMaxBlocks;
-    if (bb != qt.b) load_query<FMT>(qt, a, bb, n, G);
+    const int bh = key / kMaxBlocks, j = key - bh * kMaxBlocks;
+    if (bh != qb) {
+      qb = bh;
+#pragma unroll
+      for (int k = 0; k < NT; ++k) load_query<FMT>(qt[k], a, bh / H, NT * (bh % H) + k, n, G);
+    }
     if (s_page[i] >= 0) {
-      score_page<FMT>(buf, qt, a, j, n, G);
-    } else if (G == 0 && n < qt.ql) {
-      const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + j;
-      a.ws_score[o] = -INFINITY;
-      a.ws_bound[o] = 0.f;
+      if constexpr (NT == 1) score_page<FMT>(buf, qt[0], a, j, n, G);
+      else score_page_n<FMT, NT>(buf, qt, a, j, n, G);
+    } else if (G == 0) {
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        if (n < qt[k].ql) {
+          const int64_t o = (int64_t)(qt[k].r0 + n) * a.max_blocks + j;
+          a.ws_score[o] = -INFINITY;
+          a.ws_bound[o] = 0.f;
+        }
+      }
     }
   };
 
   for (int64_t c0 = w0; c0 < w1; c0 += kScanChunk) {  // uniform over the workgroup
     const int cnt = (int)min((int64_t)kScanChunk, w1 - c0);
     for (int i = tid; i < cnt; i += kScanWaves * 64) {
-      const int64_t u = c0 + i;
+      const int64_t u = (c0 + i) / H;  // the H passes of a block are adjacent units
+      const int half = (int)((c0 + i) - u * H);
       const int bl = req_of(u);
       const int jl = (int)(u - s_blk[bl]);
       int key = -1, pg = -1;
       if (jl < a.max_blocks) {
-        key = bl * kMaxBlocks + jl;
+        key = (bl * H + half) * kMaxBlocks + jl;
+        // rows past the query tiles' capacity are never scored: flag the group
+        if (jl == 0 && half == 0 && a.cu_q[bl + 1] - a.cu_q[bl] > 16 * NT * H) set_status(a.status, kDevBadRows);
         const int breq = a.grp_req ? a.grp_req[bl] : bl;  // the group's request
         pg = breq >= 0 ? a.block_table[(int64_t)breq * a.bt_stride + jl] : -1;
         if (pg < 0 || pg >= a.num_pages) {
@@ -390,9 +504,25 @@ __global__ __launch_bounds__(kScanWaves * 64) void index_scan_kernel(IndexArgs a
     if (tid == 0) s_ctr = 0;
     __syncthreads();
     // one page in flight per wave; the other waves of the SIMD cover its latency
+    // (measured: for the prefill variant a second page in flight per wave was
+    // slower, its time goes to the scoring itself)
     while (true) {
       const int i0 = claim();
       if (i0 >= cnt) break;
+      if constexpr (NT > 1) {
+        // a new group's query tiles are built before its page is loaded, so the
+        // page registers are not live across the build
+        const int key = s_unit[i0];
+        const int bh = key / kMaxBlocks;
+        if (key >= 0 && bh != qb) {
+          qb = bh;
+#pragma unroll
+          for (int k = 0; k < NT; ++k) {
+            load_query<FMT>(qt[k], a, bh / H, NT * (bh % H) + k, n, G);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
       if (s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
       process(pa, i0);
     }
@@ -846,14 +976,21 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t stream) {
   IndexArgs a = a0;
   if (a.num_rows == 0) return hipSuccess;
   if (a.num_reqs > 0) {
-    const int64_t units_upper = (int64_t)a.num_reqs * a.max_blocks;
-    int64_t grid = (units_upper + kScanWaves - 1) / kScanWaves;
+    const bool wide = a.group_tiles > 1;  // prefill work groups of up to 64 rows
+    const int waves = wide ? 8 : 16;
+    const int passes = wide && a.format == 2 ? 2 : 1;
+    const int64_t units_upper = (int64_t)a.num_reqs * a.max_blocks * passes;
+    int64_t grid = (units_upper + waves - 1) / waves;
     if (grid > a.scan_grid) grid = a.scan_grid;
     if (grid < 1) grid = 1;
-    if (a.format == 1)
-      hipLaunchKernelGGL(index_scan_kernel<1>, dim3((unsigned)grid), dim3(kScanWaves * 64), 0, stream, a);
-    else
-      hipLaunchKernelGGL(index_scan_kernel<2>, dim3((unsigned)grid), dim3(kScanWaves * 64), 0, stream, a);
+    const dim3 g((unsigned)grid), blk((unsigned)(waves * 64));
+    if (a.format == 1) {
+      if (wide) hipLaunchKernelGGL((index_scan_kernel<1, 4, 8, 1>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((index_scan_kernel<1, 1, 16, 1>), g, blk, 0, stream, a);
+    } else {
+      if (wide) hipLaunchKernelGGL((index_scan_kernel<2, 2, 8, 2>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((index_scan_kernel<2, 1, 16, 1>), g, blk, 0, stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -113,6 +113,7 @@ struct IndexArgs {
   float* ws_bound;   // [num_rows, max_blocks]
   uint32_t* status;
   int32_t scan_grid; // workgroups of the scan kernel
+  int32_t group_tiles; // 16-row query tiles per work group: 1 (decode, groups of <= 16 rows) or 4 (<= 64)
 };
 
 struct AttendArgs {

@@ -49,9 +49,9 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_scan, int* tot
   return excl;
 }
 
-constexpr int kGroupRows = 16;  // rows per scan work group (the MFMA tile's columns)
+constexpr int kGroupRows = 64;  // rows per scan work group (four MFMA column tiles)
 
-// Prefill row map and the scan's 16-row work groups, in one workgroup. The
+// Prefill row map and the scan's 64-row work groups, in one workgroup. The
 // request offsets, lengths and group offsets are staged in LDS; every row and
 // every group is then written by its own thread (a chunk of thousands of rows
 // is no longer one thread's loop).

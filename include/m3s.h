@@ -66,7 +66,7 @@ extern "C" {
 #define M3S_MAX_HEADS 16     /* query heads per KV head (G) */
 #define M3S_MAX_TOPK 64
 #define M3S_MAX_REQS 4096
-#define M3S_MAX_GROUPS 4096  /* scan work groups (requests, or 16-row prefill groups) */
+#define M3S_MAX_GROUPS 4096  /* scan work groups (requests, or 64-row prefill groups) */
 #define M3S_MAX_ROWS 65536
 #define M3S_MAX_BLOCKS 8192  /* causal blocks per request: 1,048,576 tokens */
 
@@ -140,10 +140,11 @@ typedef struct m3s_cache {
  * m3s_sparse_attend ([ATOM-2744] Design, Attention: one row-map launch,
  * shared by the attention and the fused top-k).
  *
- * The index scan scores one page against a work group of at most 16
- * consecutive rows of one request at a time. m3s_decode_rows makes each
- * request one group (grp_row = cu_q, grp_req = NULL); m3s_prefill_rows cuts a
- * request's rows into groups of 16.
+ * The index scan scores one page against a work group of consecutive rows of
+ * one request at a time. With grp_req = NULL (m3s_decode_rows: each request
+ * is one group, grp_row = cu_q) a group holds at most 16 rows; with grp_req
+ * set (m3s_prefill_rows: each request's rows cut into groups of 64) at most
+ * 64. Rows past that in a group are not scored and set M3S_DEV_BAD_ROWS.
  */
 typedef struct m3s_rows {
   const int32_t* grp_row; /* [num_groups + 1] first row of each work group; grp_row[num_groups] ends the rows */
@@ -257,12 +258,12 @@ m3s_status m3s_qknorm_rope_store(const m3s_cache* cache, const uint16_t* q, int6
  * token of a request's prefill chunk is a row; row r of request b sees
  *   row_len = seq_lens[b] - (cu_q[b+1] - cu_q[b]) + 1 + (r - cu_q[b])
  * tokens (the decode_rows map with no bound on a request's row count). It
- * also cuts each request's rows into work groups of 16 for the index scan:
+ * also cuts each request's rows into work groups of 64 for the index scan:
  *   grp_row int32 [max_groups + 1], grp_req int32 [max_groups],
  *   grp_blk int32 [max_groups + 1] (outputs; groups past the last real one
  *   are empty); pass them with num_groups = max_groups in m3s_rows.
- *   max_groups   in [1, M3S_MAX_GROUPS]; sum_b ceil(q_len_b / 16) groups are
- *                needed, at most ceil(cu_q[B] / 16) + num_reqs
+ *   max_groups   in [1, M3S_MAX_GROUPS]; sum_b ceil(q_len_b / 64) groups are
+ *                needed, at most ceil(cu_q[B] / 64) + num_reqs
  * A request with seq_len < q_len sets M3S_DEV_BAD_ROWS and its rows become pad
  * rows. A cu_q that does not start at 0, decreases or passes num_rows, or more
  * groups than max_groups, sets M3S_DEV_BAD_ROWS and makes every row a pad row.

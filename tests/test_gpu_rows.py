@@ -61,14 +61,14 @@ def _prefill(m3s, cu_q, seq, R, max_groups=None):
     return g(rows.row_req), g(rows.row_len), g(rows.grp_row), g(rows.grp_req), g(rows.grp_blk), int(st.item())
 
 
-def _check_groups(cu, seq, rl, gr, gq, gb):
-    """Work groups: consecutive runs of at most 16 rows of one request, in row order,
+def _check_groups(cu, seq, rl, gr, gq, gb, group_rows=64):
+    """Work groups: consecutive runs of at most 64 rows of one request, in row order,
     covering every live row once; block prefix = causal blocks of each group's last row."""
     G = len(gq)
     live = [g for g in range(G) if gq[g] >= 0]
     want_rows, nb = [], []
     for b in range(len(seq)):
-        for s0 in range(int(cu[b]), int(cu[b + 1]), 16):
+        for s0 in range(int(cu[b]), int(cu[b + 1]), group_rows):
             want_rows.append((s0, b))
     assert [(int(gr[g]), int(gq[g])) for g in live] == want_rows
     assert live == list(range(len(live)))                  # real groups first
@@ -76,7 +76,7 @@ def _check_groups(cu, seq, rl, gr, gq, gb):
         n = int(gr[g + 1] - gr[g])
         if gq[g] >= 0:
             b = int(gq[g])
-            assert 1 <= n <= 16 and gr[g] >= cu[b] and gr[g + 1] <= cu[b + 1]
+            assert 1 <= n <= group_rows and gr[g] >= cu[b] and gr[g + 1] <= cu[b + 1]
             nb.append((int(rl[gr[g + 1] - 1]) + 127) // 128 if seq[b] >= cu[b + 1] - cu[b] else 0)
         else:
             assert n == 0
@@ -110,7 +110,7 @@ def test_prefill_rows_reject(gpu):
     assert rr[:40].tolist() == [0] * 40 and rl[79] == 35
     _check_groups(cu, seq, rl, gr, gq, gb)
     # a decreasing cu_q, or too few groups: every row becomes a pad row
-    for cu, seq, R, G in (([0, 30, 20, 50], [30, 40, 50], 50, None), ([0, 40, 80], [40, 80], 80, 4)):
+    for cu, seq, R, G in (([0, 30, 20, 50], [30, 40, 50], 50, None), ([0, 70, 80], [70, 80], 80, 2)):
         rr, rl, gr, gq, gb, st = _prefill(gpu, cu, seq, R, G)
         assert st & bad_bit
         assert np.all(rr == -1) and np.all(rl == 0) and gb[-1] == 0 and np.all(gq == -1)
