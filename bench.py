@@ -1,8 +1,10 @@
 """Throughput of the decode hot path (store + decode_rows + index score/top-k + sparse
 attend) on one MI355X, on seeded synthetic inputs shaped like the pages' workloads.
 
-One step = one sparse layer's full path for one batch: m3s_store of the step's new
-K/V/index rows, m3s_decode_rows, m3s_index_topk, m3s_sparse_attend. Steps are HIP-graph
+One step = one sparse layer's full path for one batch: the store of the step's new
+K/V/index rows, the row map, the index top-k and the sparse attention, issued as
+m3s_store_and_rows + m3s_index_topk_attend (or, with --separate, as the four calls
+m3s_store, m3s_decode_rows, m3s_index_topk, m3s_sparse_attend). Steps are HIP-graph
 replays; consecutive steps use different layer copies of the cache (8 by default, >= 2 GB
 in total at the default workload) so a step cannot be served from the 256 MB Infinity
 Cache left warm by the previous one - as in a real model, where each of the 60 sparse
@@ -223,7 +225,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--separate", action="store_true",
-                    help="call m3s_store and m3s_decode_rows separately (default: m3s_store_and_rows, one launch)")
+                    help="one call per stage: m3s_store, m3s_decode_rows, m3s_index_topk, m3s_sparse_attend "
+                         "(default: m3s_store_and_rows and m3s_index_topk_attend)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB float32 copy kernel (torch.neg) whose HBM bytes are known, "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -301,7 +304,9 @@ def main():
     ws_i = m3s.index_workspace(rows, lay.max_blocks, cfg.topk, dev)
     ws_a = m3s.attend_workspace(rows, lay.max_blocks, cfg.topk, G, dev)
 
+    ws_f = m3s.index_attend_workspace(rows, lay.max_blocks, cfg.topk, G, dev)
     fused_front = not prefill and not args.separate
+    fused_attend = not args.separate
 
     def run_step(c):
         if fused_front:
@@ -309,8 +314,12 @@ def main():
         else:
             m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
             row_map()
-        m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0, ids, ws_i, status)
-        m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids, cfg.sm_scale, out, ws_a, status)
+        if fused_attend:
+            m3s.m3s_index_topk_attend(c, case.q_idx, case.q, bt, lay.max_blocks, rows, cfg.topk, cfg.sm_scale, 0,
+                                      ids, out, ws_f, status)
+        else:
+            m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0, ids, ws_i, status)
+            m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids, cfg.sm_scale, out, ws_a, status)
 
     for c in caches:  # eager warm-up, checks the status word
         run_step(c)
@@ -374,7 +383,10 @@ def main():
               ("index_topk", lambda c: m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0,
                                                            ids, ws_i, status)),
               ("sparse_attend", lambda c: m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids,
-                                                                 cfg.sm_scale, out, ws_a, status))]
+                                                                 cfg.sm_scale, out, ws_a, status)),
+              ("index_topk_attend", lambda c: m3s.m3s_index_topk_attend(c, case.q_idx, case.q, bt, lay.max_blocks,
+                                                                         rows, cfg.topk, cfg.sm_scale, 0, ids, out,
+                                                                         ws_f, status))]
     if not prefill:
         # the fused producer store (norm + rotary + FP4 store + query rows) for the step's new
         # tokens, beside the plain store of the same rows, each into its own one-page cache
@@ -474,7 +486,8 @@ def main():
         "config": {"workload": cfg.name, "requests": len(lay.seq_lens), "rows_per_request": cfg.q_len,
                    "context": [int(x) for x in sorted(set(lay.seq_lens.tolist()))][:4],
                    "heads_per_kv_head": G, "topk": cfg.topk, "cache_format": cfg.fmt, "layers_cycled": NL,
-                   "front": "m3s_store_and_rows" if fused_front else "separate store and row-map calls"},
+                   "front": "m3s_store_and_rows" if fused_front else "separate store and row-map calls",
+                   "topk_attend": "m3s_index_topk_attend" if fused_attend else "separate m3s_index_topk, m3s_sparse_attend"},
         "hbm_gbs_step": round(gbs_step, 1),
         "bytes_per_step": by["total"],
         "stage_us": None if not stage_ms else {nm: round(v * 1e3, 2) for (nm, _), v in zip(stages, stage_ms)},

@@ -7,7 +7,7 @@ the path runs in the library's HIP kernels. Loading fails loudly when the
 library is missing: there is no fallback.
 
 Functions carry the C names: m3s_store, m3s_decode_rows, m3s_store_and_rows, m3s_prefill_rows,
-m3s_qknorm_rope_store, m3s_index_topk, m3s_sparse_attend, m3s_workspace_bytes,
+m3s_qknorm_rope_store, m3s_index_topk, m3s_sparse_attend, m3s_index_topk_attend, m3s_workspace_bytes,
 m3s_read_device_status, m3s_status_string, m3s_version.
 """
 from __future__ import annotations
@@ -25,7 +25,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 FMT_NVFP4, FMT_MXFP4 = 1, 2
 FORMATS = {"nvfp4": FMT_NVFP4, "mxfp4": FMT_MXFP4}
 SCALE_BYTES = {FMT_NVFP4: 8, FMT_MXFP4: 4}
-OP_INDEX_TOPK, OP_SPARSE_ATTEND = 1, 2
+OP_INDEX_TOPK, OP_SPARSE_ATTEND, OP_INDEX_TOPK_ATTEND = 1, 2, 3
 TOPK_TIE_HIGH_ID = 1
 DEV_BITS = {
     "BAD_SLOT": 1 << 0, "BAD_ROWS": 1 << 1, "BAD_LENGTH": 1 << 2, "BAD_PAGE": 1 << 3,
@@ -33,7 +33,7 @@ DEV_BITS = {
 }
 
 EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_qknorm_rope_store",
-           "m3s_index_topk", "m3s_sparse_attend",
+           "m3s_index_topk", "m3s_sparse_attend", "m3s_index_topk_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
 MAX_GROUPS = 4096
 GROUP_ROWS = 64
@@ -85,6 +85,8 @@ def load(path: str | None = None):
                                         V, V, V, V, V]),
         "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, I32, I32, V, V, SZ, V, V]),
         "m3s_sparse_attend": (I32, [V, V, I64, I64, I32, V, I32, I32, V, V, I32, F32, V, V, SZ, V, V]),
+        "m3s_index_topk_attend": (I32, [V, V, I64, V, I64, I64, I32, V, I32, I32, V, I32, I32, I32, I32, F32, V, V,
+                                        V, SZ, V, V]),
         "m3s_workspace_bytes": (SZ, [I32, I32, I32, I32, I32, I32]),
         "m3s_read_device_status": (I32, [V, V, V]),
         "m3s_status_string": (ctypes.c_char_p, [I32]),
@@ -377,6 +379,43 @@ def m3s_sparse_attend(cache: Cache, q, block_table, max_blocks: int, rows: Rows,
                                   _ptr(dev_status), _stream(stream))
     _check("m3s_sparse_attend", st)
     return out
+
+
+def index_attend_workspace(rows: Rows, max_blocks: int, topk: int, num_heads: int, device="cuda"):
+    torch = _torch()
+    n = m3s_workspace_bytes(OP_INDEX_TOPK_ATTEND, rows.num_rows, rows.num_reqs, max_blocks, topk, num_heads)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def m3s_index_topk_attend(cache: Cache, q_idx, q, block_table, max_blocks: int, rows: Rows, topk: int,
+                          sm_scale: float, flags: int = 0, topk_ids=None, out=None, workspace=None, dev_status=None,
+                          stream=None, init_blocks: int = 0, local_blocks: int = 0):
+    """m3s_index_topk then m3s_sparse_attend on its ids, select and attention split fused.
+    Returns (topk_ids, out)."""
+    torch = _torch()
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(q, "q", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    if q_idx.dim() != 2 or q_idx.stride(1) != 1 or q_idx.shape[1] < HEAD_DIM:
+        raise ValueError("q_idx must be [R, >=128] with unit inner stride")
+    if q.dim() != 3 or q.stride(2) != 1 or q.shape[2] < HEAD_DIM:
+        raise ValueError("q must be [R, G, >=128] with unit inner stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, stride] with unit inner stride")
+    G = q.shape[1]
+    dev = q.device
+    if topk_ids is None:
+        topk_ids = torch.empty((rows.num_rows, topk), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((rows.num_rows, G, HEAD_DIM), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = index_attend_workspace(rows, max_blocks, topk, G, dev)
+    st = load().m3s_index_topk_attend(cache.ref(), _ptr(q_idx), q_idx.stride(0), _ptr(q), q.stride(0), q.stride(1), G,
+                                      _ptr(block_table), block_table.stride(0), max_blocks, rows.ref(), topk, flags,
+                                      init_blocks, local_blocks, float(sm_scale), _ptr(topk_ids), _ptr(out),
+                                      _ptr(workspace), workspace.numel(), _ptr(dev_status), _stream(stream))
+    _check("m3s_index_topk_attend", st)
+    return topk_ids, out
 
 
 def m3s_read_device_status(dev_status, stream=None) -> int:

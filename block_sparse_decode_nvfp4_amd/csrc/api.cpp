@@ -84,6 +84,8 @@ size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32
   if (num_rows < 0 || max_blocks < 0 || topk < 1 || topk > M3S_MAX_TOPK) return 0;
   if (op == M3S_OP_INDEX_TOPK) return index_ws_bytes(num_rows, max_blocks);
   if (op == M3S_OP_SPARSE_ATTEND) return attend_ws_bytes(num_rows, attend_nsplit(topk));
+  if (op == M3S_OP_INDEX_TOPK_ATTEND)
+    return ((index_ws_bytes(num_rows, max_blocks) + 255) & ~(size_t)255) + attend_ws_bytes(num_rows, attend_nsplit(topk));
   return 0;
 }
 
@@ -263,11 +265,17 @@ m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_
   return from_hip(launch_prefill_rows(a, stream));
 }
 
-m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
-                          const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, const m3s_rows* rows,
-                          int32_t topk, int32_t flags, int32_t init_blocks, int32_t local_blocks,
-                          int32_t* topk_ids, void* workspace, size_t workspace_bytes,
-                          uint32_t* dev_status, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Validation and argument set-up of the index call; workspace as given.
+m3s_status index_args(IndexArgs& a, const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                      const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, const m3s_rows* rows,
+                      int32_t topk, int32_t flags, int32_t init_blocks, int32_t local_blocks, int32_t* topk_ids,
+                      void* workspace, size_t workspace_bytes, uint32_t* dev_status) {
   m3s_status st = check_cache(cache);
   if (st != M3S_OK) return st;
   if (!cache->idx_data || !cache->idx_scale) return M3S_ERR_INVALID_ARG;
@@ -285,8 +293,6 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
   }
   const size_t need = index_ws_bytes(rows->num_rows, max_blocks);
   if (workspace_bytes < need || (need > 0 && !workspace) || !aligned16(workspace)) return M3S_ERR_WORKSPACE;
-  if (rows->num_rows == 0) return M3S_OK;
-  IndexArgs a;
   a.format = cache->format;
   a.idx_data = cache->idx_data;
   a.idx_scale = cache->idx_scale;
@@ -311,15 +317,16 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
   a.ws_score = static_cast<float*>(workspace);
   a.ws_bound = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
   a.status = dev_status;
-  a.scan_grid = scan_grid();
+  a.scan_grid = rows->num_rows > 0 ? scan_grid() : 0;
   a.group_tiles = rows->grp_req ? 4 : 1;
-  return from_hip(launch_index_topk(a, stream));
+  return M3S_OK;
 }
 
-m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
-                             int32_t num_heads, const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
-                             const m3s_rows* rows, const int32_t* topk_ids, int32_t topk, float sm_scale, float* out,
-                             void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
+// Validation and argument set-up of the attention; workspace as given.
+m3s_status attend_args(AttendArgs& a, const m3s_cache* cache, const uint16_t* q, int64_t q_row_stride,
+                       int64_t q_head_stride, int32_t num_heads, const int32_t* block_table, int32_t bt_stride,
+                       int32_t max_blocks, const m3s_rows* rows, const int32_t* topk_ids, int32_t topk,
+                       float sm_scale, float* out, void* workspace, size_t workspace_bytes, uint32_t* dev_status) {
   m3s_status st = check_cache(cache);
   if (st != M3S_OK) return st;
   if (!cache->k_data || !cache->k_scale || !cache->v_data || !cache->v_scale) return M3S_ERR_INVALID_ARG;
@@ -339,8 +346,6 @@ m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t 
   const int32_t nsplit = attend_nsplit(topk);
   const size_t need = attend_ws_bytes(rows->num_rows, nsplit);
   if (workspace_bytes < need || (need > 0 && !workspace) || !aligned16(workspace)) return M3S_ERR_WORKSPACE;
-  if (rows->num_rows == 0) return M3S_OK;
-  AttendArgs a;
   a.format = cache->format;
   a.k_data = cache->k_data;
   a.k_scale = cache->k_scale;
@@ -362,11 +367,61 @@ m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t 
   a.nsplit = nsplit;
   a.sm_scale = sm_scale;
   a.out = out;
-  const size_t po = ((size_t)rows->num_rows * nsplit * 16 * M3S_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255;
+  const size_t po = align256((size_t)rows->num_rows * nsplit * 16 * M3S_HEAD_DIM * sizeof(float));
   a.part_o = static_cast<float*>(workspace);
   a.part_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + po) : nullptr;
   a.status = dev_status;
+  return M3S_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                          const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, const m3s_rows* rows,
+                          int32_t topk, int32_t flags, int32_t init_blocks, int32_t local_blocks,
+                          int32_t* topk_ids, void* workspace, size_t workspace_bytes,
+                          uint32_t* dev_status, hipStream_t stream) {
+  IndexArgs a;
+  const m3s_status st = index_args(a, cache, q_idx, q_idx_stride, block_table, bt_stride, max_blocks, rows, topk,
+                                   flags, init_blocks, local_blocks, topk_ids, workspace, workspace_bytes, dev_status);
+  if (st != M3S_OK || rows->num_rows == 0) return st;
+  return from_hip(launch_index_topk(a, stream));
+}
+
+m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                             int32_t num_heads, const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                             const m3s_rows* rows, const int32_t* topk_ids, int32_t topk, float sm_scale, float* out,
+                             void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
+  AttendArgs a;
+  const m3s_status st = attend_args(a, cache, q, q_row_stride, q_head_stride, num_heads, block_table, bt_stride,
+                                    max_blocks, rows, topk_ids, topk, sm_scale, out, workspace, workspace_bytes,
+                                    dev_status);
+  if (st != M3S_OK || rows->num_rows == 0) return st;
   return from_hip(launch_sparse_attend(a, stream));
+}
+
+m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                                 const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride, int32_t num_heads,
+                                 const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                                 const m3s_rows* rows, int32_t topk, int32_t flags, int32_t init_blocks,
+                                 int32_t local_blocks, float sm_scale, int32_t* topk_ids, float* out,
+                                 void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
+  if (!rows) return M3S_ERR_INVALID_ARG;
+  if (max_blocks < 0 || rows->num_rows < 0) return M3S_ERR_INVALID_ARG;
+  const size_t ni = align256(index_ws_bytes(rows->num_rows, max_blocks));
+  if (workspace_bytes < ni) return M3S_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  IndexArgs ia;
+  m3s_status st = index_args(ia, cache, q_idx, q_idx_stride, block_table, bt_stride, max_blocks, rows, topk, flags,
+                             init_blocks, local_blocks, topk_ids, ws, ni, dev_status);
+  if (st != M3S_OK) return st;
+  AttendArgs aa;
+  st = attend_args(aa, cache, q, q_row_stride, q_head_stride, num_heads, block_table, bt_stride, max_blocks, rows,
+                   topk_ids, topk, sm_scale, out, ws ? ws + ni : nullptr, workspace_bytes - ni, dev_status);
+  if (st != M3S_OK || rows->num_rows == 0) return st;
+  return from_hip(launch_index_topk_attend(ia, aa, stream));
 }
 
 m3s_status m3s_read_device_status(const uint32_t* dev_status, uint32_t* out, hipStream_t stream) {

@@ -40,6 +40,7 @@
 
 #include "fp4.hpp"
 #include "launch.hpp"
+#include "attend_body.hpp"
 
 namespace m3s {
 
@@ -602,6 +603,7 @@ struct SelectShared {
   int cnt[4];  // candidates, in, band, selected
   uint64_t keys[2];
   int sel[64];
+  int selp[64];  // page of each gathered id (when the caller wants pages)
 };
 
 // bitonic network over one u32 per lane, descending across the wave
@@ -623,13 +625,20 @@ __device__ __forceinline__ uint32_t bitonic32_sizes(uint32_t x) {
   else return bitonic32_sizes<SIZE * 2>(bitonic32_steps<SIZE, SIZE / 2>(x));
 }
 
-template <int FMT, int PER>
-__global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
+// The select of row r as a device function, for a workgroup of NW waves (4 or
+// 8). The first four waves hold the row's blocks (thread t < 256: blocks
+// t + 256 i) and run every phase; further waves take part only in the exact
+// rescore (one band block per wave) and in the barriers. It writes the row's
+// ids to topk_ids when write_ids. When ids_out is given, wave 0 also leaves
+// the sorted ids and their pages in ids_out / pages_out and the row's request
+// and length in row_out (LDS, visible after the caller's next barrier).
+template <int FMT, int PER, int NW, bool PAGES>
+__device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShared& sh, bool write_ids,
+                                           int* ids_out, int* pages_out, int* row_out) {
   constexpr int SB = FMT == 1 ? 8 : 4;
   constexpr int kSelPer = PER;
-  __shared__ SelectShared sh;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = blockIdx.x;
+  const int bt0 = tid < 256 ? tid : (1 << 30);  // first block of the thread; none past the fourth wave
   const int k = a.topk;
   const int th = a.tie_high;
   const int MB = a.max_blocks;
@@ -643,7 +652,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   float sv[kSelPer], bv[kSelPer];
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int j = tid + 256 * i;
+    const int j = bt0 + 256 * i;
     if (j >= MB) break;
     sv[i] = sc[j];
     bv[i] = bd[j];
@@ -651,17 +660,26 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   uint32_t qbits = 0;
   if (tid < kDim) qbits = a.q_idx[(int64_t)r * a.q_stride + tid];
   const int nb = (len + kPage - 1) / kPage;
+  if (PAGES && tid == 0) {
+    row_out[0] = b;
+    row_out[1] = len;
+  }
   if (b < 0 || len <= 0 || nb > MB || nb <= k) {
     if (b >= 0 && (len <= 0 || nb > MB) && tid == 0) set_status(a.status, kDevBadLength);
     const bool all = b >= 0 && len > 0 && nb <= MB;
-    if (tid < k) out[tid] = (all && tid < nb) ? tid : -1;
+    const int id = (all && tid < nb) ? tid : -1;
+    if (write_ids && tid < k) out[tid] = id;
+    if (PAGES && tid < k) {
+      ids_out[tid] = id;
+      pages_out[tid] = id >= 0 ? a.block_table[(int64_t)b * a.bt_stride + id] : -1;
+    }
     return;
   }
   int pv[kSelPer];
   const int32_t* btr = a.block_table + (int64_t)b * a.bt_stride;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int j = tid + 256 * i;
+    const int j = bt0 + 256 * i;
     if (j >= nb) break;
     pv[i] = btr[j];
   }
@@ -673,7 +691,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   float dm = 0.f;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int j = tid + 256 * i;
+    const int j = bt0 + 256 * i;
     if (j >= MB) break;
     if (j >= nb) sv[i] = -INFINITY;
     else if (cls_of(j) == 0) dm = fmaxf(dm, bv[i]);
@@ -684,20 +702,20 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   uint32_t ok[kSelPer];
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int j = tid + 256 * i;
+    const int j = bt0 + 256 * i;
     if (j >= nb) break;
     const int c = cls_of(j);
     ok[i] = c == 2 ? 0xFFFFFFFFu : (c == 1 ? 0xFFFFFFFEu : ord_f32(sv[i]));
   }
   auto forced = [&](int i) { return ok[i] >= 0xFFFFFFFEu; };
   auto okey = [&](int i) { return ok[i]; };
-  auto ckey = [&](int i) { return comp_key(ok[i], tid + 256 * i, forced(i) ? 1 : th); };
+  auto ckey = [&](int i) { return comp_key(ok[i], bt0 + 256 * i, forced(i) ? 1 : th); };
 
   // 1. threshold from the per-wave sorted thread maxima
   uint32_t tmax = 0;
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int j = tid + 256 * i;
+    const int j = bt0 + 256 * i;
     if (j >= nb) break;
     tmax = max(tmax, okey(i));
   }
@@ -734,7 +752,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     const uint32_t srt = bitonic32_sizes<2>(tmax);
     if (cw > 0) theta_w = __shfl(srt, cw - 1, 64);
   }
-  if (lane == 0) {
+  if (lane == 0 && w < 4) {
     sh.red[w] = dm;
     sh.ired[w] = lqv;
     sh.thr[w] = theta_w;
@@ -748,7 +766,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     const uint32_t theta = min(min(sh.thr[0], sh.thr[1]), min(sh.thr[2], sh.thr[3]));
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
-      const int j = tid + 256 * i;
+      const int j = bt0 + 256 * i;
       if (j >= nb) break;
       if (okey(i) >= theta) {
         const int slot = atomicAdd(&sh.cnt[0], 1);
@@ -773,7 +791,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       uint64_t best = 0;
 #pragma unroll
       for (int i = 0; i < kSelPer; ++i) {
-        const int j = tid + 256 * i;
+        const int j = bt0 + 256 * i;
         if (j >= nb) break;
         const uint64_t c = ckey(i);
         if (c < prev && c > best) best = c;
@@ -804,7 +822,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     int nin = 0;
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
-      const int j = tid + 256 * i;
+      const int j = bt0 + 256 * i;
       if (j >= nb) break;
       const double s_ = (double)sv[i];
       if (forced(i) || s_ > hi) {
@@ -842,7 +860,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       QueryTile qt;
       build_query<FMT>(qt, a, n == 0 ? r : -1, n, G);  // column 0: this row
       const double2 qq = *reinterpret_cast<const double2*>(&sh.q[2 * lane]);
-      for (int m = w; m < nband; m += 4) {
+      for (int m = w; m < nband; m += NW) {
         const int j = sh.band[m];
         const int page = sh.bpage[m];
         double best = -INFINITY;
@@ -927,7 +945,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
       }
       if (inexact) set_status(a.status, kDevInexact);
       __syncthreads();
-      for (int i = tid; i < nband; i += 256) {
+      for (int i = tid; i < nband; i += 64 * NW) {
         const double ei = sh.dots[i] + 0.0;
         const int ji = sh.band[i];
         const uint32_t ki = th ? (uint32_t)ji : ~(uint32_t)ji;
@@ -940,7 +958,10 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
         }
         if (rank < need) {
           const int slot = atomicAdd(&sh.cnt[3], 1);
-          if (slot < 64) sh.sel[slot] = ji;
+          if (slot < 64) {
+            sh.sel[slot] = ji;
+            if (PAGES) sh.selp[slot] = sh.bpage[i];
+          }
         }
       }
     }
@@ -948,7 +969,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   // 3. the selected ids, gathered and sorted ascending by one wave
 #pragma unroll
   for (int i = 0; i < kSelPer; ++i) {
-    const int j = tid + 256 * i;
+    const int j = bt0 + 256 * i;
     if (j >= nb) break;
     bool in;
     if (mode == 0) in = ckey(i) >= Kk;
@@ -956,15 +977,58 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
     else in = forced(i) || (double)sv[i] > hi;
     if (in) {
       const int slot = atomicAdd(&sh.cnt[3], 1);
-      if (slot < 64) sh.sel[slot] = j;
+      if (slot < 64) {
+        sh.sel[slot] = j;
+        if (PAGES) sh.selp[slot] = pv[i];
+      }
     }
   }
   __syncthreads();
   if (w != 0) return;
   const int nsel = min(sh.cnt[3], 64);
-  const uint32_t y = lane < nsel ? ~(uint32_t)sh.sel[lane] : 0u;  // descending ~id = ascending id
-  const uint32_t srt = bitonic32_sizes<2>(y);
-  if (lane < k) out[lane] = lane < nsel ? (int)~srt : -1;
+  if constexpr (PAGES) {
+    // (~id, page) pairs sorted descending: ascending ids with their pages
+    const uint64_t y = lane < nsel ? ((uint64_t)~(uint32_t)sh.sel[lane] << 32) | (uint32_t)sh.selp[lane] : 0u;
+    const uint64_t srt = wave_sort_desc(y);
+    const int id = lane < nsel ? (int)~(uint32_t)(srt >> 32) : -1;
+    if (lane < k) {
+      if (write_ids) out[lane] = id;
+      ids_out[lane] = id;
+      pages_out[lane] = lane < nsel ? (int)(uint32_t)srt : -1;
+    }
+  } else {
+    const uint32_t y = lane < nsel ? ~(uint32_t)sh.sel[lane] : 0u;  // descending ~id = ascending id
+    const uint32_t srt = bitonic32_sizes<2>(y);
+    if (write_ids && lane < k) out[lane] = lane < nsel ? (int)~srt : -1;
+  }
+}
+
+template <int FMT, int PER>
+__global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
+  __shared__ SelectShared sh;
+  select_row<FMT, PER, 4, false>(a, blockIdx.x, sh, true, nullptr, nullptr, nullptr);
+}
+
+// Top-k and attention split in one workgroup of 8 waves per (row, split): the
+// row's select runs in every split's workgroup (the first split also writes the
+// ids), and the split then attends its blocks with the ids, their pages and
+// the row's request and length already on chip. This removes a kernel boundary
+// and the attention's two dependent loads (ids, then pages) before its K / V
+// loads. The select's LDS is reused by the attention once the ids are out.
+union SelectAttendShared {
+  SelectShared s;
+  AttendShared t;
+};
+
+template <int FMT, int PER>
+__global__ __launch_bounds__(kWaves * 64) void select_attend_kernel(IndexArgs ia, AttendArgs aa) {
+  __shared__ SelectAttendShared u;
+  __shared__ int s_ids[64], s_pages[64], s_row[2];
+  const int r = blockIdx.x / aa.nsplit;
+  const int sp = blockIdx.x - r * aa.nsplit;
+  select_row<FMT, PER, kWaves, true>(ia, r, u.s, sp == 0, s_ids, s_pages, s_row);
+  __syncthreads();
+  attend_split_body<FMT>(aa, r, sp, u.t, s_ids, s_pages, s_row[0], s_row[1]);
 }
 
 size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks) {
@@ -972,9 +1036,7 @@ size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks) {
   return 2 * one;
 }
 
-hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t stream) {
-  IndexArgs a = a0;
-  if (a.num_rows == 0) return hipSuccess;
+static hipError_t launch_scan(const IndexArgs& a, hipStream_t stream) {
   if (a.num_reqs > 0) {
     const bool wide = a.group_tiles > 1;  // prefill work groups of up to 64 rows
     const int waves = wide ? 8 : 16;
@@ -991,9 +1053,15 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t stream) {
       if (wide) hipLaunchKernelGGL((index_scan_kernel<2, 2, 8, 2>), g, blk, 0, stream, a);
       else hipLaunchKernelGGL((index_scan_kernel<2, 1, 16, 1>), g, blk, 0, stream, a);
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    return hipGetLastError();
   }
+  return hipSuccess;
+}
+
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  hipError_t e = launch_scan(a, stream);
+  if (e != hipSuccess) return e;
   const dim3 g((unsigned)a.num_rows), blk(256);
   if (a.max_blocks <= 256 * 8) {
     if (a.format == 1) hipLaunchKernelGGL((index_select_kernel<1, 8>), g, blk, 0, stream, a);
@@ -1006,6 +1074,26 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t stream) {
     else hipLaunchKernelGGL((index_select_kernel<2, 32>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream) {
+  if (ia.num_rows == 0) return hipSuccess;
+  hipError_t e = launch_scan(ia, stream);
+  if (e != hipSuccess) return e;
+  const dim3 g((unsigned)((int64_t)ia.num_rows * aa.nsplit)), blk(kWaves * 64);
+  if (ia.max_blocks <= 256 * 8) {
+    if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 8>), g, blk, 0, stream, ia, aa);
+    else hipLaunchKernelGGL((select_attend_kernel<2, 8>), g, blk, 0, stream, ia, aa);
+  } else if (ia.max_blocks <= 256 * 16) {
+    if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 16>), g, blk, 0, stream, ia, aa);
+    else hipLaunchKernelGGL((select_attend_kernel<2, 16>), g, blk, 0, stream, ia, aa);
+  } else {
+    if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 32>), g, blk, 0, stream, ia, aa);
+    else hipLaunchKernelGGL((select_attend_kernel<2, 32>), g, blk, 0, stream, ia, aa);
+  }
+  e = hipGetLastError();
+  if (e != hipSuccess || aa.nsplit == 1) return e;
+  return launch_attend_combine(aa, stream);
 }
 
 }  // namespace m3s

@@ -150,6 +150,8 @@ hipError_t launch_store_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t 
 hipError_t launch_producer(const ProducerArgs& a, hipStream_t stream);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream);
+hipError_t launch_attend_combine(const AttendArgs& a, hipStream_t stream);
 
 // Workspace layout helpers shared by sizing and launching.
 size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks);

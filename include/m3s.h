@@ -337,8 +337,29 @@ m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t 
                              float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                              uint32_t* dev_status, hipStream_t stream);
 
+/*
+ * m3s_index_topk_attend - m3s_index_topk followed by m3s_sparse_attend on its
+ * ids, with the select and the attention's split pass in one kernel
+ * ([ATOM-2744] review notes: the fused top-k carries the splits and their
+ * merge). Each (row, split) workgroup selects the row's blocks itself and then
+ * attends its share of them with the ids and pages still on chip: one kernel
+ * boundary and the attention's dependent id and page loads fewer than the two
+ * calls. Arguments, validation, outputs (topk_ids and out) and status bits are
+ * those of the two calls, bit for bit; the select runs once per split, so a
+ * row's status bits may be set more than once.
+ *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_INDEX_TOPK_ATTEND, ...)
+ *                (the index call's part, then the attention's, each 256-byte aligned)
+ */
+m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                                 const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                                 int32_t num_heads, const int32_t* block_table, int32_t bt_stride,
+                                 int32_t max_blocks, const m3s_rows* rows, int32_t topk, int32_t flags,
+                                 int32_t init_blocks, int32_t local_blocks, float sm_scale,
+                                 int32_t* topk_ids, float* out, void* workspace, size_t workspace_bytes,
+                                 uint32_t* dev_status, hipStream_t stream);
+
 /* Workspace sizing (host only, pure). */
-enum { M3S_OP_INDEX_TOPK = 1, M3S_OP_SPARSE_ATTEND = 2 };
+enum { M3S_OP_INDEX_TOPK = 1, M3S_OP_SPARSE_ATTEND = 2, M3S_OP_INDEX_TOPK_ATTEND = 3 };
 size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32_t max_blocks,
                            int32_t topk, int32_t num_heads);
 

@@ -223,3 +223,33 @@ def test_qknorm_rope_store_validation(lib):
     assert f(qs=511) == I and f(G=4, qs=504) == I and f(rs=120) == I and f(rs=132) == I
     assert f(pos=None) == I and f(cs=None) == I and f(mp=0) == I
     assert f(cache=m3s.m3s_cache(1, 4, 128, 128, 1, 4096, 4096, None, 4096, 4096, 4096)) == I
+
+
+def test_index_topk_attend_validation(lib):
+    """The fused call validates as the two calls do and launches nothing here."""
+    I, U, Wk = m3s.ERR_INVALID_ARG, m3s.ERR_UNSUPPORTED, m3s.ERR_WORKSPACE
+    rows = _rows(nreq=1, nrows=2)
+    big = 1 << 30
+
+    def f(cache=None, qi=FAKE, qis=128, q=FAKE, qrs=2048, qhs=128, G=16, bt=FAKE, bts=64, mb=64, r=rows, k=16,
+          flags=0, ini=0, loc=0, sm=1.0, ids=FAKE, out=FAKE, ws=FAKE, wsb=big):
+        c = _cache() if cache is None else cache
+        return lib.m3s_index_topk_attend(ctypes.byref(c), qi, qis, q, qrs, qhs, G, bt, bts, mb,
+                                         None if r is None else ctypes.byref(r), k, flags, ini, loc, sm, ids, out, ws,
+                                         wsb, None, None)
+
+    assert f(r=None) == I
+    assert f(cache=_cache(fmt=7)) == U
+    assert f(k=0) == U and f(k=65) == U
+    assert f(G=0) == U and f(G=17) == U
+    assert f(flags=2) == I and f(ini=-1) == I
+    assert f(sm=float("nan")) == I
+    assert f(qi=None) == I and f(q=None) == I and f(ids=None) == I and f(out=None) == I
+    assert f(qis=100) == I and f(qrs=12) == I
+    assert f(bt=None) == I and f(bts=10) == I
+    assert f(ws=None) == Wk and f(wsb=0) == Wk
+    need = m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK_ATTEND, 2, 1, 64, 16, 16)
+    assert need == ((m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 2, 1, 64, 16, 16) + 255) // 256) * 256 + \
+        m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 2, 1, 64, 16, 16)
+    assert f(wsb=need - 1) == Wk
+    assert f(r=_rows(nreq=0, nrows=0)) == m3s.OK        # no rows: nothing to do

@@ -1,0 +1,104 @@
+"""m3s_index_topk_attend (select and attention split in one kernel) against the two
+separate calls on the same inputs: ids and outputs bit for bit, status included, over
+decode and prefill rows, both formats, forced blocks, the tie rule, pad rows, one and
+many splits, and the select's three register widths; one case also against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from tests.stepcase import run_gpu_step, oracle_requests, max_rel_err, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+CFG0 = W.config(0)
+
+
+def _pad(t, R):
+    if R <= t.shape[0]:
+        return t
+    return torch.cat([t, torch.zeros((R - t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)])
+
+
+def _fused(gpu, step, topk, sm_scale, flags=0, init_blocks=0, local_blocks=0, workspace_junk=True):
+    R = step.ids.shape[0]
+    qi, q = _pad(step.case.q_idx, R), _pad(step.case.q, R)
+    G = q.shape[1]
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ws = gpu.index_attend_workspace(step.rows, step.case.layout.max_blocks, topk, G, DEV)
+    if workspace_junk:
+        ws.fill_(0x7F)
+    ids = torch.full((R, topk), -9, dtype=torch.int32, device=DEV)
+    out = torch.full((R, G, 128), float("nan"), dtype=torch.float32, device=DEV)
+    gpu.m3s_index_topk_attend(step.cache, qi, q, step.bt, step.case.layout.max_blocks, step.rows, topk, sm_scale,
+                              flags=flags, topk_ids=ids, out=out, workspace=ws, dev_status=st,
+                              init_blocks=init_blocks, local_blocks=local_blocks)
+    torch.cuda.synchronize()
+    return ids, out, int(st.item())
+
+
+CASES = [
+    # fmt, seq_lens, q_len, G, topk, flags, init, local, prefill, extra pad rows
+    ("nvfp4", [150_000, 3000, 40_000], 8, 16, 16, 0, 0, 0, False, 3),
+    ("mxfp4", [150_000, 3000, 40_000], 8, 16, 16, 0, 0, 0, False, 0),
+    ("nvfp4", [20_000, 700, 9000], [4, 1, 8], 4, 4, 0, 0, 0, False, 2),      # one split
+    ("nvfp4", [20_000, 9000], 3, 8, 64, 1, 0, 0, False, 0),                  # 16 splits, higher-id ties
+    ("mxfp4", [30_000, 12_000, 800], 2, 2, 16, 0, 4, 16, False, 1),         # forced blocks
+    ("nvfp4", [30_000, 5000], [300, 40], 4, 8, 0, 0, 0, True, 0),           # prefill rows
+    ("nvfp4", [500_000], 2, 2, 16, 0, 0, 0, False, 0),                      # 3907 blocks: 16 per thread
+    ("mxfp4", [1_000_000], 2, 2, 16, 0, 0, 0, False, 0),                    # 7813 blocks: 32 per thread
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-k{c[4]}-{i}" for i, c in enumerate(CASES)])
+def test_fused_equals_separate_calls(gpu, case):
+    fmt, seq, ql, G, topk, flags, init, local, prefill, npad = case
+    say(f"[fused] {case}")
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
+    R = int(wc.layout.cu_q[-1]) + npad
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, fmt=fmt, flags=flags, sm_scale=0.3, num_rows=R, case=wc,
+                        init_blocks=init, local_blocks=local, prefill=prefill)
+    assert step.status == 0, hex(step.status)
+    ids, out, st = _fused(gpu, step, topk, 0.3, flags, init, local)
+    assert st == step.status
+    assert torch.equal(ids, step.ids)
+    assert torch.equal(out, step.out)
+
+
+def test_fused_against_oracle(gpu):
+    """Ids exact and attention within 5e-3 of the oracle, directly."""
+    seq, ql, G, topk = [40_000, 2000, 9000], 8, 8, 16
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc)
+    ids, out, st = _fused(gpu, step, topk, 0.3)
+    assert st == 0
+    want_ids, want_out, _, _ = oracle_requests(step, "nvfp4", topk, 0.3, range(len(seq)))
+    got = ids.cpu().numpy()
+    o = out.cpu().double().numpy()
+    worst = 0.0
+    for r, w in want_ids.items():
+        assert got[r].tolist() == w.tolist(), r
+        worst = max(worst, max_rel_err(o[r], want_out[r]))
+    assert worst <= 5e-3, worst
+
+
+def test_fused_invalid_pages_flagged(gpu):
+    """A selected block whose page is outside the cache is skipped and flagged, as in
+    the separate attention; ids are unchanged."""
+    seq, ql, G, topk = [20_000, 6000], 4, 4, 8
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc)
+    bad_blk = int(step.ids[0, 0].item())
+    bt = step.bt.clone()
+    bt[0, bad_blk] = step.case.layout.num_pages + 3
+    step.bt = bt
+    R = step.ids.shape[0]
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids_s = gpu.m3s_index_topk(step.cache, step.case.q_idx, bt, step.case.layout.max_blocks, step.rows, topk,
+                               dev_status=st)
+    out_s = gpu.m3s_sparse_attend(step.cache, step.case.q, bt, step.case.layout.max_blocks, step.rows, ids_s, 0.3,
+                                  dev_status=st)
+    torch.cuda.synchronize()
+    ids, out, st_f = _fused(gpu, step, topk, 0.3)
+    assert st_f == int(st.item()) and st_f & gpu.DEV_BITS["BAD_PAGE"]
+    assert torch.equal(ids, ids_s) and torch.equal(out, out_s)
