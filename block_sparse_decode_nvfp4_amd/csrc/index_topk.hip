@@ -1058,10 +1058,7 @@ static hipError_t launch_scan(const IndexArgs& a, hipStream_t stream) {
   return hipSuccess;
 }
 
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream) {
-  if (a.num_rows == 0) return hipSuccess;
-  hipError_t e = launch_scan(a, stream);
-  if (e != hipSuccess) return e;
+static hipError_t launch_select(const IndexArgs& a, hipStream_t stream) {
   const dim3 g((unsigned)a.num_rows), blk(256);
   if (a.max_blocks <= 256 * 8) {
     if (a.format == 1) hipLaunchKernelGGL((index_select_kernel<1, 8>), g, blk, 0, stream, a);
@@ -1076,11 +1073,27 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream) {
+  if (a.num_rows == 0) return hipSuccess;
+  hipError_t e = launch_scan(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_select(a, stream);
+}
+
 hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream) {
   if (ia.num_rows == 0) return hipSuccess;
   hipError_t e = launch_scan(ia, stream);
   if (e != hipSuccess) return e;
-  const dim3 g((unsigned)((int64_t)ia.num_rows * aa.nsplit)), blk(kWaves * 64);
+  const int64_t wgs = (int64_t)ia.num_rows * aa.nsplit;
+  if (wgs > 2 * (int64_t)ia.scan_grid) {
+    // Many rows (prefill): every split's workgroup would repeat its row's select,
+    // which only pays while the launch is latency-bound (measured at a 4096-row
+    // chunk: twice the time of the separate kernels). Same results either way.
+    e = launch_select(ia, stream);
+    if (e != hipSuccess) return e;
+    return launch_sparse_attend(aa, stream);
+  }
+  const dim3 g((unsigned)wgs), blk(kWaves * 64);
   if (ia.max_blocks <= 256 * 8) {
     if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 8>), g, blk, 0, stream, ia, aa);
     else hipLaunchKernelGGL((select_attend_kernel<2, 8>), g, blk, 0, stream, ia, aa);

@@ -1,7 +1,9 @@
 """m3s_index_topk_attend (select and attention split in one kernel) against the two
 separate calls on the same inputs: ids and outputs bit for bit, status included, over
 decode and prefill rows, both formats, forced blocks, the tie rule, pad rows, one and
-many splits, and the select's three register widths; one case also against the oracle."""
+many splits, and the select's three register widths; one case also against the oracle.
+Launches of more than two workgroups per CU take the separate kernels inside the call
+(the 340-row prefill case); every other case runs the fused kernel."""
 import numpy as np
 import pytest
 import torch
@@ -44,7 +46,8 @@ CASES = [
     ("nvfp4", [20_000, 700, 9000], [4, 1, 8], 4, 4, 0, 0, 0, False, 2),      # one split
     ("nvfp4", [20_000, 9000], 3, 8, 64, 1, 0, 0, False, 0),                  # 16 splits, higher-id ties
     ("mxfp4", [30_000, 12_000, 800], 2, 2, 16, 0, 4, 16, False, 1),         # forced blocks
-    ("nvfp4", [30_000, 5000], [300, 40], 4, 8, 0, 0, 0, True, 0),           # prefill rows
+    ("nvfp4", [30_000, 5000], [300, 40], 4, 8, 0, 0, 0, True, 0),           # prefill rows (separate kernels)
+    ("mxfp4", [30_000, 5000], [100, 20], 4, 8, 0, 0, 0, True, 0),           # prefill rows (fused kernel)
     ("nvfp4", [500_000], 2, 2, 16, 0, 0, 0, False, 0),                      # 3907 blocks: 16 per thread
     ("mxfp4", [1_000_000], 2, 2, 16, 0, 0, 0, False, 0),                    # 7813 blocks: 32 per thread
 ]
