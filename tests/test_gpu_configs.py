@@ -1,6 +1,7 @@
-"""The full step on every workload configuration, in the launch configuration the bench
-times: ids bit-exact and attention within 5e-3 of the oracle on sampled requests (all of
-their rows), stored planes bit-exact on those requests' pages."""
+"""The full step on every workload configuration: ids bit-exact and attention within 5e-3
+of the oracle on sampled requests (all of their rows), stored planes bit-exact on those
+requests' pages; and the call the bench times (m3s_index_topk_attend) equal to the
+separate calls bit for bit on every row."""
 import numpy as np
 import pytest
 import torch
@@ -36,6 +37,13 @@ def test_config_full_step(gpu, ci):
         worst = max(worst, max_rel_err(got[r], outs[r]))
     say(f"[config {cfg.name}] ids equal on {len(ids)} rows, max rel err {worst:.2e}")
     assert worst <= TOL
+    # the bench's call: select and attention fused, on the same inputs, bit for bit
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids_f, out_f = gpu.m3s_index_topk_attend(step.cache, step.case.q_idx, step.case.q, step.bt, lay.max_blocks,
+                                             step.rows, cfg.topk, cfg.sm_scale, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(ids_f, step.ids) and torch.equal(out_f, step.out)
     # stored planes of the sampled requests (index plane: every page; K/V: the new rows' pages)
     sb = 8 if cfg.fmt == "nvfp4" else 4
     for b in reqs:

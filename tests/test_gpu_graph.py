@@ -29,12 +29,14 @@ def _fill_history(m3s, fmt, lay, case):
     return cache, slots[new_idx].contiguous(), new_idx
 
 
-@pytest.mark.parametrize("fmt,prefill", [("nvfp4", False), ("mxfp4", False), ("nvfp4", True), ("mxfp4", True)])
-def test_step_graph_replays_match_eager(gpu, fmt, prefill):
+@pytest.mark.parametrize("fmt,prefill,fused", [("nvfp4", False, False), ("mxfp4", False, False),
+                                               ("nvfp4", True, False), ("mxfp4", True, False),
+                                               ("nvfp4", False, True), ("mxfp4", True, True)])
+def test_step_graph_replays_match_eager(gpu, fmt, prefill, fused):
     seq = [3000, 9000, 20000]
     ql = [200, 70, 1] if prefill else [4, 8, 1]
     G, topk = 8, 8
-    say(f"[graph] step fmt={fmt} prefill={prefill}")
+    say(f"[graph] step fmt={fmt} prefill={prefill} fused={fused}")
     case = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
     lay = case.layout
     R = int(lay.cu_q[-1]) + 3                       # three pad rows
@@ -57,6 +59,7 @@ def test_step_graph_replays_match_eager(gpu, fmt, prefill):
     out = torch.empty((R, G, 128), dtype=torch.float32, device=DEV)
     ws_i = gpu.index_workspace(rows, lay.max_blocks, topk, DEV)
     ws_a = gpu.attend_workspace(rows, lay.max_blocks, topk, G, DEV)
+    ws_f = gpu.index_attend_workspace(rows, lay.max_blocks, topk, G, DEV)
 
     def step():
         if prefill:
@@ -65,8 +68,11 @@ def test_step_graph_replays_match_eager(gpu, fmt, prefill):
         else:
             gpu.m3s_store_and_rows(cache, k_new, v_new, i_new, s_new, cu_q, seq_t, R, row_req, row_len, req_blk,
                                    status)
-        gpu.m3s_index_topk(cache, q_idx, bt, lay.max_blocks, rows, topk, 0, ids, ws_i, status)
-        gpu.m3s_sparse_attend(cache, q, bt, lay.max_blocks, rows, ids, 0.3, out, ws_a, status)
+        if fused:
+            gpu.m3s_index_topk_attend(cache, q_idx, q, bt, lay.max_blocks, rows, topk, 0.3, 0, ids, out, ws_f, status)
+        else:
+            gpu.m3s_index_topk(cache, q_idx, bt, lay.max_blocks, rows, topk, 0, ids, ws_i, status)
+            gpu.m3s_sparse_attend(cache, q, bt, lay.max_blocks, rows, ids, 0.3, out, ws_a, status)
 
     step()
     torch.cuda.synchronize()
@@ -79,7 +85,7 @@ def test_step_graph_replays_match_eager(gpu, fmt, prefill):
     with torch.cuda.graph(g, stream=side):
         step()
     torch.cuda.synchronize()
-    junk = [ids, out, ws_i, ws_a, rows.row_req, rows.row_len, rows.grp_blk]
+    junk = [ids, out, ws_i, ws_a, ws_f, rows.row_req, rows.row_len, rows.grp_blk]
     if prefill:
         junk += [rows.grp_row, rows.grp_req]
     else:
