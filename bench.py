@@ -367,6 +367,23 @@ def main():
     ms_per_step = ms_total / args.steps
     st = int(status.item())
 
+    # ---- per-replay distribution: an event between consecutive replays, the whole run
+    # queued behind a GPU spin so that the host's enqueue rate does not show; the events'
+    # own cost lands inside the intervals, so these read slightly above ms_per_step
+    nd = min(args.steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nd + 1)]
+    torch.cuda._sleep(20_000_000)
+    evs[0].record()
+    for i in range(nd):
+        graphs[i % NL].replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_us = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(nd))
+
+    def pct(f):
+        return round(per_us[min(nd - 1, int(round(f * (nd - 1))))], 2)
+    step_dist = {"replays": nd, "p10": pct(0.1), "median": pct(0.5), "p90": pct(0.9)}
+
     # ---- per-stage HIP-event times. Events cannot be recorded inside a captured graph on
     # ROCm, so each stage is launched eagerly, args.stage_reps times back to back (cycling
     # the layer caches), between two events on the stream it runs on; a GPU spin first lets
@@ -430,6 +447,8 @@ def main():
     rows_per_s = R / (ms_per_step / 1e3)
     gbs_step = by["total"] / (ms_per_step / 1e3) / 1e9
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (event), wall {wall / args.steps * 1e6:.2f} us/step")
+    log(f"[bench] per replay ({nd} replays, events between them): p10 {step_dist['p10']:.2f}, "
+        f"median {step_dist['median']:.2f}, p90 {step_dist['p90']:.2f} us")
     log(f"[bench] algorithmic bytes/step: index {by['index'] / 1e6:.2f} MB, attend {by['attend'] / 1e6:.2f} MB, "
         f"other {by['other'] / 1e6:.2f} MB, total {by['total'] / 1e6:.2f} MB -> {gbs_step:.0f} GB/s")
     roofline = None
@@ -489,6 +508,7 @@ def main():
                    "front": "m3s_store_and_rows" if fused_front else "separate store and row-map calls",
                    "topk_attend": "m3s_index_topk_attend" if fused_attend else "separate m3s_index_topk, m3s_sparse_attend"},
         "hbm_gbs_step": round(gbs_step, 1),
+        "step_us_dist": step_dist,
         "bytes_per_step": by["total"],
         "stage_us": None if not stage_ms else {nm: round(v * 1e3, 2) for (nm, _), v in zip(stages, stage_ms)},
         "device_status": st,
