@@ -559,15 +559,24 @@ __device__ __forceinline__ uint64_t bitonic_steps(uint64_t x) {
     return bitonic_steps<SIZE, STRIDE / 2>(x);
   }
 }
-template <int SIZE>
+// Sizes 2 .. MAX: each group of MAX lanes ends sorted, the first group
+// (lanes 0 .. MAX - 1) descending.
+template <int SIZE, int MAX = 64>
 __device__ __forceinline__ uint64_t bitonic_sizes(uint64_t x) {
-  if constexpr (SIZE > 64) {
+  if constexpr (SIZE > MAX) {
     return x;
   } else {
-    return bitonic_sizes<SIZE * 2>(bitonic_steps<SIZE, SIZE / 2>(x));
+    return bitonic_sizes<SIZE * 2, MAX>(bitonic_steps<SIZE, SIZE / 2>(x));
   }
 }
 __device__ __forceinline__ uint64_t wave_sort_desc(uint64_t x) { return bitonic_sizes<2>(x); }
+// Descending sort of the first n lanes' keys (the other lanes hold 0): a
+// network over only the lanes that can hold keys.
+__device__ __forceinline__ uint64_t sort_desc_first(uint64_t x, int n) {
+  if (n <= 16) return bitonic_sizes<2, 16>(x);
+  if (n <= 32) return bitonic_sizes<2, 32>(x);
+  return bitonic_sizes<2>(x);
+}
 
 // Select: one 256-thread workgroup per row.
 //   0. the row's scores (thread t holds blocks j = t + 256 i), its largest
@@ -619,10 +628,10 @@ __device__ __forceinline__ uint32_t bitonic32_steps(uint32_t x) {
     return bitonic32_steps<SIZE, STRIDE / 2>(x);
   }
 }
-template <int SIZE>
+template <int SIZE, int MAX = 64>
 __device__ __forceinline__ uint32_t bitonic32_sizes(uint32_t x) {
-  if constexpr (SIZE > 64) return x;
-  else return bitonic32_sizes<SIZE * 2>(bitonic32_steps<SIZE, SIZE / 2>(x));
+  if constexpr (SIZE > MAX) return x;
+  else return bitonic32_sizes<SIZE * 2, MAX>(bitonic32_steps<SIZE, SIZE / 2>(x));
 }
 
 // The select of row r as a device function, for a workgroup of NW waves (4 or
@@ -778,7 +787,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShar
   const int ncand = sh.cnt[0];
   if (small_k && ncand <= 64) {
     if (w == 0) {
-      const uint64_t srt = wave_sort_desc(lane < ncand ? sh.cand[lane] : 0);
+      const uint64_t srt = sort_desc_first(lane < ncand ? sh.cand[lane] : 0, ncand);
       const uint64_t Kk = shfl_u64(srt, k - 1), K1 = shfl_u64(srt, k);
       if (lane == 0) {
         sh.keys[0] = Kk;
@@ -989,7 +998,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShar
   if constexpr (PAGES) {
     // (~id, page) pairs sorted descending: ascending ids with their pages
     const uint64_t y = lane < nsel ? ((uint64_t)~(uint32_t)sh.sel[lane] << 32) | (uint32_t)sh.selp[lane] : 0u;
-    const uint64_t srt = wave_sort_desc(y);
+    const uint64_t srt = sort_desc_first(y, nsel);
     const int id = lane < nsel ? (int)~(uint32_t)(srt >> 32) : -1;
     if (lane < k) {
       if (write_ids) out[lane] = id;
@@ -998,7 +1007,7 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShar
     }
   } else {
     const uint32_t y = lane < nsel ? ~(uint32_t)sh.sel[lane] : 0u;  // descending ~id = ascending id
-    const uint32_t srt = bitonic32_sizes<2>(y);
+    const uint32_t srt = nsel <= 16 ? bitonic32_sizes<2, 16>(y) : bitonic32_sizes<2>(y);
     if (write_ids && lane < k) out[lane] = lane < nsel ? (int)~srt : -1;
   }
 }
