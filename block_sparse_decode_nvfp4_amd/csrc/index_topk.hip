@@ -828,14 +828,19 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShar
   if (dmax > 0.f && (uint32_t)(Kk >> 32) < 0xFFFFFFFEu) {
     lo = (double)unord_f32((uint32_t)(Kk >> 32)) - 2.0 * (double)dmax;
     hi = (double)unord_f32((uint32_t)(K1 >> 32)) + 2.0 * (double)dmax;
-    int nin = 0;
+    // the certain blocks are gathered here (fewer than k: the k-th key is not
+    // forced, and only the top k keys can clear hi), the band is listed
 #pragma unroll
     for (int i = 0; i < kSelPer; ++i) {
       const int j = bt0 + 256 * i;
       if (j >= nb) break;
       const double s_ = (double)sv[i];
       if (forced(i) || s_ > hi) {
-        ++nin;
+        const int slot = atomicAdd(&sh.cnt[3], 1);
+        if (slot < 64) {
+          sh.sel[slot] = j;
+          if (PAGES) sh.selp[slot] = pv[i];
+        }
       } else if (s_ >= lo) {
         const int slot = atomicAdd(&sh.cnt[2], 1);
         if (slot < kBandCap) {
@@ -845,16 +850,24 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShar
         }
       }
     }
-    nin = lane_sum<1, 64>(nin);
-    if (lane == 0 && nin) atomicAdd(&sh.cnt[1], nin);
     __syncthreads();
-    const int need = k - sh.cnt[1];
+    const int nin = sh.cnt[3];
+    const int need = k - nin;
     const int nband = sh.cnt[2];
     if (nband == need) {
-      mode = 1;
+      mode = 1;  // the band fills the open slots: appended after the certain blocks
+      for (int i = tid; i < nband; i += 64 * NW) {
+        if (nin + i < 64) {
+          sh.sel[nin + i] = sh.band[i];
+          if (PAGES) sh.selp[nin + i] = sh.bpage[i];
+        }
+      }
     } else if (nband > kBandCap) {
       if (tid == 0) set_status(a.status, kDevBandOverflow);
-      mode = 0;
+      mode = 0;  // selected by key below, from an empty list
+      __syncthreads();  // every thread has read the counts
+      if (tid == 0) sh.cnt[3] = 0;
+      __syncthreads();
     } else {
       mode = 2;
       // exact rescore, one band block per wave. The wave first re-scores the
@@ -975,20 +988,19 @@ __device__ __forceinline__ void select_row(const IndexArgs& a, int r, SelectShar
       }
     }
   }
-  // 3. the selected ids, gathered and sorted ascending by one wave
+  // 3. the selected ids (gathered above when certified, else by key here),
+  // sorted ascending by one wave
+  if (mode == 0) {
 #pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    const int j = bt0 + 256 * i;
-    if (j >= nb) break;
-    bool in;
-    if (mode == 0) in = ckey(i) >= Kk;
-    else if (mode == 1) in = forced(i) || (double)sv[i] >= lo;
-    else in = forced(i) || (double)sv[i] > hi;
-    if (in) {
-      const int slot = atomicAdd(&sh.cnt[3], 1);
-      if (slot < 64) {
-        sh.sel[slot] = j;
-        if (PAGES) sh.selp[slot] = pv[i];
+    for (int i = 0; i < kSelPer; ++i) {
+      const int j = bt0 + 256 * i;
+      if (j >= nb) break;
+      if (ckey(i) >= Kk) {
+        const int slot = atomicAdd(&sh.cnt[3], 1);
+        if (slot < 64) {
+          sh.sel[slot] = j;
+          if (PAGES) sh.selp[slot] = pv[i];
+        }
       }
     }
   }
