@@ -75,6 +75,30 @@ def test_index_equal_blocks_need_exact_rescore(gpu):
     _check_all(gpu, step, "nvfp4", 16)
 
 
+def test_index_band_overflow_selects_by_key(gpu):
+    """More than 1024 blocks tie exactly (every page holds the same tokens) and the fp32
+    error bound is non-zero, so the band exceeds the rescore's capacity. The select then
+    takes the k best fp32 keys (identical pages give identical fp32 scores, so ties go to
+    the lower ids) and reports M3S_DEV_BAND_OVERFLOW. The ids still equal the exact
+    selection, through m3s_index_topk and through the fused m3s_index_topk_attend."""
+    nblk = 1100
+    case = W.make_case(CFG0, DEV, seq_lens=[128 * nblk], q_len=2, G=2)
+    lay = case.layout
+    n = int(lay.seq_lens[0])
+    base = case.idx[:128].clone()
+    case.idx[:n] = base.repeat(nblk, 1)[:n]
+    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case)
+    assert step.status == gpu.DEV_BITS["BAND_OVERFLOW"], hex(step.status)
+    _check_all(gpu, step, "nvfp4", 16)
+    assert step.ids.cpu().numpy().tolist() == [list(range(16))] * 2
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids_f, _ = gpu.m3s_index_topk_attend(step.cache, case.q_idx, case.q, step.bt, lay.max_blocks, step.rows, 16,
+                                         1.0, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == gpu.DEV_BITS["BAND_OVERFLOW"], hex(int(st.item()))
+    assert torch.equal(ids_f, step.ids)
+
+
 def test_index_near_ties_are_decided_exactly(gpu):
     """Blocks that differ from block 0 by a single tiny element: exact scores differ far
     below the fp32 error bound, so the selection is decided by the float64 rescore."""
