@@ -60,6 +60,14 @@ int scan_grid() {
 
 m3s_status from_hip(hipError_t e) { return e == hipSuccess ? M3S_OK : M3S_ERR_HIP; }
 
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Fused call's workspace: the index call's part, the attention's, then the
+// selected ids' pages, each 256-byte aligned. Offset of the last part.
+size_t fused_ws_pages_offset(int32_t num_rows, int32_t max_blocks, int32_t topk) {
+  return align256(index_ws_bytes(num_rows, max_blocks)) + align256(attend_ws_bytes(num_rows, attend_nsplit(topk)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,7 +93,7 @@ size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32
   if (op == M3S_OP_INDEX_TOPK) return index_ws_bytes(num_rows, max_blocks);
   if (op == M3S_OP_SPARSE_ATTEND) return attend_ws_bytes(num_rows, attend_nsplit(topk));
   if (op == M3S_OP_INDEX_TOPK_ATTEND)
-    return ((index_ws_bytes(num_rows, max_blocks) + 255) & ~(size_t)255) + attend_ws_bytes(num_rows, attend_nsplit(topk));
+    return fused_ws_pages_offset(num_rows, max_blocks, topk) + align256((size_t)num_rows * topk * sizeof(int32_t));
   return 0;
 }
 
@@ -269,8 +277,6 @@ m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_
 
 namespace {
 
-size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-
 // Validation and argument set-up of the index call; workspace as given.
 m3s_status index_args(IndexArgs& a, const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
                       const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, const m3s_rows* rows,
@@ -314,6 +320,7 @@ m3s_status index_args(IndexArgs& a, const m3s_cache* cache, const uint16_t* q_id
   a.init_blocks = init_blocks;
   a.local_blocks = local_blocks;
   a.topk_ids = topk_ids;
+  a.sel_pages = nullptr;
   a.ws_score = static_cast<float*>(workspace);
   a.ws_bound = reinterpret_cast<float*>(static_cast<char*>(workspace) + need / 2);
   a.status = dev_status;
@@ -363,6 +370,7 @@ m3s_status attend_args(AttendArgs& a, const m3s_cache* cache, const uint16_t* q,
   a.row_len = rows->row_len;
   a.num_rows = rows->num_rows;
   a.topk_ids = topk_ids;
+  a.sel_pages = nullptr;
   a.topk = topk;
   a.nsplit = nsplit;
   a.sm_scale = sm_scale;
@@ -421,6 +429,14 @@ m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, 
   st = attend_args(aa, cache, q, q_row_stride, q_head_stride, num_heads, block_table, bt_stride, max_blocks, rows,
                    topk_ids, topk, sm_scale, out, ws ? ws + ni : nullptr, workspace_bytes - ni, dev_status);
   if (st != M3S_OK || rows->num_rows == 0) return st;
+  // The last part holds the page of each selected id, written by the select
+  // beside the ids when the call runs the select and the attention as
+  // separate kernels (many rows); the attention then skips its block-table
+  // lookup.
+  const size_t np = fused_ws_pages_offset(rows->num_rows, max_blocks, topk);
+  if (workspace_bytes < np + align256((size_t)rows->num_rows * topk * sizeof(int32_t))) return M3S_ERR_WORKSPACE;
+  ia.sel_pages = reinterpret_cast<int32_t*>(ws + np);
+  aa.sel_pages = ia.sel_pages;
   return from_hip(launch_index_topk_attend(ia, aa, stream));
 }
 

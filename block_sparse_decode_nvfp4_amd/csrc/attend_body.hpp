@@ -46,9 +46,11 @@ __device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
 }
 
 // Split (row r, split sp) of the attention, run by kWaves waves. The selected
-// block ids come from topk_ids and their pages from the block table, or, when
-// s_ids is given (the select ran in the same workgroup), the ids, their pages
-// and the row's request and length come from the caller (LDS / registers).
+// block ids come from topk_ids and their pages from the block table, or from
+// sel_pages when the select wrote them (loaded beside the ids: no dependent
+// lookup), or, when s_ids is given (the select ran in the same workgroup), the
+// ids, their pages and the row's request and length come from the caller (LDS /
+// registers).
 template <int FMT>
 __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, int sp, AttendShared& sh,
                                                   const int* s_ids, const int* s_pages, int b_in, int len_in) {
@@ -64,6 +66,7 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
   const int b = s_ids ? b_in : a.row_req[r];
   const int len = s_ids ? len_in : a.row_len[r];
   const int id = slot < a.topk ? (s_ids ? s_ids[slot] : a.topk_ids[(int64_t)r * a.topk + slot]) : -1;
+  const int pg_sel = (!s_ids && a.sel_pages && slot < a.topk) ? a.sel_pages[(int64_t)r * a.topk + slot] : -1;
   u32x4 raw[4] = {};
   if (n < a.num_heads) {
     const uint16_t* qp = a.q + (int64_t)r * a.q_row_stride + (int64_t)n * a.q_head_stride + 32 * G;
@@ -77,7 +80,8 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
       if (id >= nbr || id >= a.max_blocks) {
         if (lane == 0) set_status(a.status, kDevBadBlockId);
       } else {
-        const int pg = s_ids ? s_pages[slot] : a.block_table[(int64_t)b * a.bt_stride + id];
+        const int pg = s_ids ? s_pages[slot]
+                             : (a.sel_pages ? pg_sel : a.block_table[(int64_t)b * a.bt_stride + id]);
         if (pg < 0 || pg >= a.num_pages) {
           if (lane == 0) set_status(a.status, kDevBadPage);
         } else {

@@ -1030,6 +1030,18 @@ __global__ __launch_bounds__(256) void index_select_kernel(IndexArgs a) {
   select_row<FMT, PER, 4, false>(a, blockIdx.x, sh, true, nullptr, nullptr, nullptr);
 }
 
+// The same select, also writing each selected id's page to sel_pages, for an
+// attention pass launched after it (its K / V addresses then need no
+// block-table lookup).
+template <int FMT, int PER>
+__global__ __launch_bounds__(256) void index_select_pages_kernel(IndexArgs a) {
+  __shared__ SelectShared sh;
+  __shared__ int s_row[2];
+  const int r = blockIdx.x;
+  select_row<FMT, PER, 4, true>(a, r, sh, false, a.topk_ids + (int64_t)r * a.topk,
+                                a.sel_pages + (int64_t)r * a.topk, s_row);
+}
+
 // Top-k and attention split in one workgroup of 8 waves per (row, split): the
 // row's select runs in every split's workgroup (the first split also writes the
 // ids), and the split then attends its blocks with the ids, their pages and
@@ -1081,7 +1093,18 @@ static hipError_t launch_scan(const IndexArgs& a, hipStream_t stream) {
 
 static hipError_t launch_select(const IndexArgs& a, hipStream_t stream) {
   const dim3 g((unsigned)a.num_rows), blk(256);
-  if (a.max_blocks <= 256 * 8) {
+  if (a.sel_pages) {
+    if (a.max_blocks <= 256 * 8) {
+      if (a.format == 1) hipLaunchKernelGGL((index_select_pages_kernel<1, 8>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((index_select_pages_kernel<2, 8>), g, blk, 0, stream, a);
+    } else if (a.max_blocks <= 256 * 16) {
+      if (a.format == 1) hipLaunchKernelGGL((index_select_pages_kernel<1, 16>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((index_select_pages_kernel<2, 16>), g, blk, 0, stream, a);
+    } else {
+      if (a.format == 1) hipLaunchKernelGGL((index_select_pages_kernel<1, 32>), g, blk, 0, stream, a);
+      else hipLaunchKernelGGL((index_select_pages_kernel<2, 32>), g, blk, 0, stream, a);
+    }
+  } else if (a.max_blocks <= 256 * 8) {
     if (a.format == 1) hipLaunchKernelGGL((index_select_kernel<1, 8>), g, blk, 0, stream, a);
     else hipLaunchKernelGGL((index_select_kernel<2, 8>), g, blk, 0, stream, a);
   } else if (a.max_blocks <= 256 * 16) {

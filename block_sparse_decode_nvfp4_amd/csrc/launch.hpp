@@ -109,6 +109,7 @@ struct IndexArgs {
   int32_t init_blocks;   // forced initial blocks per row
   int32_t local_blocks;  // forced newest blocks per row
   int32_t* topk_ids;
+  int32_t* sel_pages;  // [num_rows, topk]: page of each selected id beside topk_ids, or null
   float* ws_score;   // [num_rows, max_blocks]
   float* ws_bound;   // [num_rows, max_blocks]
   uint32_t* status;
@@ -134,6 +135,7 @@ struct AttendArgs {
   const int32_t* row_len;
   int32_t num_rows;
   const int32_t* topk_ids;
+  const int32_t* sel_pages;  // [num_rows, topk]: page of each id, written by the select; null: block table
   int32_t topk;
   int32_t nsplit;
   float sm_scale;

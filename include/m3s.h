@@ -348,7 +348,11 @@ m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t 
  * those of the two calls, bit for bit; the select runs once per split, so a
  * row's status bits may be set more than once.
  *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_INDEX_TOPK_ATTEND, ...)
- *                (the index call's part, then the attention's, each 256-byte aligned)
+ *                (the index call's part, the attention's, then the selected ids'
+ *                pages as num_rows x topk int32, each 256-byte aligned; the pages
+ *                are written when many rows make the call run the select and the
+ *                attention as separate kernels, and let the attention skip its
+ *                block-table lookup)
  */
 m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
                                  const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,

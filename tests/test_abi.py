@@ -249,7 +249,9 @@ def test_index_topk_attend_validation(lib):
     assert f(bt=None) == I and f(bts=10) == I
     assert f(ws=None) == Wk and f(wsb=0) == Wk
     need = m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK_ATTEND, 2, 1, 64, 16, 16)
-    assert need == ((m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 2, 1, 64, 16, 16) + 255) // 256) * 256 + \
-        m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 2, 1, 64, 16, 16)
+    a256 = lambda n: (n + 255) // 256 * 256
+    # the index call's part, the attention's, then 2 x 16 int32 pages of the selected ids
+    assert need == a256(m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK, 2, 1, 64, 16, 16)) + \
+        a256(m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 2, 1, 64, 16, 16)) + 256
     assert f(wsb=need - 1) == Wk
     assert f(r=_rows(nreq=0, nrows=0)) == m3s.OK        # no rows: nothing to do

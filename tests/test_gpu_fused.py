@@ -2,8 +2,9 @@
 separate calls on the same inputs: ids and outputs bit for bit, status included, over
 decode and prefill rows, both formats, forced blocks, the tie rule, pad rows, one and
 many splits, and the select's three register widths; one case also against the oracle.
-Launches of more than two workgroups per CU take the separate kernels inside the call
-(the 340-row prefill case); every other case runs the fused kernel."""
+Launches of more than two workgroups per CU take the separate kernels inside the call,
+the select then writing each selected id's page for the attention (the 340-row prefill
+cases and the 163-row decode case); every other case runs the fused kernel."""
 import numpy as np
 import pytest
 import torch
@@ -48,6 +49,8 @@ CASES = [
     ("mxfp4", [30_000, 12_000, 800], 2, 2, 16, 0, 4, 16, False, 1),         # forced blocks
     ("nvfp4", [30_000, 5000], [300, 40], 4, 8, 0, 0, 0, True, 0),           # prefill rows (separate kernels)
     ("mxfp4", [30_000, 5000], [100, 20], 4, 8, 0, 0, 0, True, 0),           # prefill rows (fused kernel)
+    ("mxfp4", [30_000, 600], [300, 40], 4, 8, 0, 0, 0, True, 0),            # separate kernels; 5-block rows
+    ("nvfp4", [4000, 900, 150_000, 20_000] * 5, 8, 16, 16, 0, 0, 0, False, 3),  # 163 decode rows: separate
     ("nvfp4", [500_000], 2, 2, 16, 0, 0, 0, False, 0),                      # 3907 blocks: 16 per thread
     ("mxfp4", [1_000_000], 2, 2, 16, 0, 0, 0, False, 0),                    # 7813 blocks: 32 per thread
 ]
@@ -85,12 +88,15 @@ def test_fused_against_oracle(gpu):
     assert worst <= 5e-3, worst
 
 
-def test_fused_invalid_pages_flagged(gpu):
+@pytest.mark.parametrize("ql,prefill", [(4, False), ([300, 40], True)], ids=["fused-kernel", "separate-kernels"])
+def test_fused_invalid_pages_flagged(gpu, ql, prefill):
     """A selected block whose page is outside the cache is skipped and flagged, as in
-    the separate attention; ids are unchanged."""
-    seq, ql, G, topk = [20_000, 6000], 4, 4, 8
+    the separate attention; ids are unchanged. With 340 rows the call runs the
+    separate kernels and the page comes from the select's page list."""
+    seq, G, topk = [20_000, 6000], 4, 8
+    say(f"[fused invalid page] q_len {ql}")
     wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
-    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc, prefill=prefill)
     bad_blk = int(step.ids[0, 0].item())
     bt = step.bt.clone()
     bt[0, bad_blk] = step.case.layout.num_pages + 3
