@@ -111,3 +111,28 @@ def test_fused_invalid_pages_flagged(gpu, ql, prefill):
     ids, out, st_f = _fused(gpu, step, topk, 0.3)
     assert st_f == int(st.item()) and st_f & gpu.DEV_BITS["BAD_PAGE"]
     assert torch.equal(ids, ids_s) and torch.equal(out, out_s)
+
+
+def test_many_rows_three_wave_select(gpu):
+    """More rows than two select workgroups per CU (520 prefill rows of one 300,000-token
+    request: 2344 blocks, 16 per thread) take the NVFP4 select built for three waves per
+    SIMD, in m3s_index_topk and, with the page list, in the fused call: ids of sampled
+    rows bit-exact against the oracle, and the fused call's ids and outputs bit for bit
+    those of the separate calls."""
+    from oracle import formats as F
+    from oracle import path as P
+    seq, ql, topk = [300_000], [520], 16
+    say("[many rows] 520 prefill rows, 300000 tokens")
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=2)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc, prefill=True)
+    assert step.status == 0, hex(step.status)
+    ids, out, st = _fused(gpu, step, topk, 0.3)
+    assert st == 0
+    assert torch.equal(ids, step.ids) and torch.equal(out, step.out)
+    _, row_len = P.decode_rows(wc.layout.cu_q, wc.layout.seq_lens, 520)
+    qi = F.bf16_to_f64(W.bf16_bits(wc.q_idx))
+    kidx = F.dequantize("nvfp4", *F.quantize("nvfp4", W.bf16_bits(wc.idx[:seq[0]])))
+    got = step.ids.cpu().numpy()
+    for r in (0, 261, 519):
+        want = P.topk_blocks(P.block_scores(qi[r], kidx, int(row_len[r])), topk, False, 0, 0)
+        assert got[r].tolist() == want.tolist(), r
