@@ -28,8 +28,13 @@ namespace m3s {
 template <int FMT>
 __global__ __launch_bounds__(kWaves * 64) void attend_split_kernel(AttendArgs a) {
   __shared__ AttendShared sh;
-  const int r = blockIdx.x / a.nsplit;
-  const int sp = blockIdx.x - r * a.nsplit;
+  int r, sp;
+  if (a.xcd_rows) {
+    row_split_of(blockIdx.x, a.nsplit, a.num_rows, r, sp);
+  } else {
+    r = blockIdx.x / a.nsplit;
+    sp = blockIdx.x - r * a.nsplit;
+  }
   attend_split_body<FMT>(a, r, sp, sh, nullptr, nullptr, 0, 0);
 }
 

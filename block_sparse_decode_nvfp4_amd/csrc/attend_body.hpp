@@ -45,6 +45,28 @@ __device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
   return __builtin_bit_cast(f16x4, r);
 }
 
+// Workgroup b of a (row, split) grid -> its row and split, with all splits of a
+// row on one XCD. The 8 XCDs take a launch's workgroups round-robin, so rows are
+// dealt in groups of 8, one row per XCD, its splits 8 workgroups apart. A row's
+// splits then share that XCD's L2 for the row's common inputs, and the combine
+// workgroup of row r (workgroup r: XCD r mod 8) finds the row's partials there.
+// Rows past the last full group of 8 take the plain row-major order. Used by the
+// split kernel when all its workgroups are resident at once (xcd_rows).
+__device__ __forceinline__ void row_split_of(int b, int nsplit, int num_rows, int& r, int& sp) {
+  const int grp = 8 * nsplit;
+  const int full = num_rows >> 3;
+  const int g = b / grp;
+  if (g < full) {
+    const int o = b - g * grp;
+    r = 8 * g + (o & 7);
+    sp = o >> 3;
+  } else {
+    const int t = b - full * grp;
+    r = 8 * full + t / nsplit;
+    sp = t - (t / nsplit) * nsplit;
+  }
+}
+
 // Split (row r, split sp) of the attention, run by kWaves waves. The selected
 // block ids come from topk_ids and their pages from the block table, or from
 // sel_pages when the select wrote them (loaded beside the ids: no dependent

@@ -138,6 +138,7 @@ struct AttendArgs {
   const int32_t* sel_pages;  // [num_rows, topk]: page of each id, written by the select; null: block table
   int32_t topk;
   int32_t nsplit;
+  int32_t xcd_rows;  // nonzero: the split kernel deals a row's splits to one XCD
   float sm_scale;
   float* out;
   float* part_o;   // [num_rows, nsplit, 16, 128]
