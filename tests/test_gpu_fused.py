@@ -136,3 +136,36 @@ def test_many_rows_three_wave_select(gpu):
     for r in (0, 261, 519):
         want = P.topk_blocks(P.block_scores(qi[r], kidx, int(row_len[r])), topk, False, 0, 0)
         assert got[r].tolist() == want.tolist(), r
+
+
+def test_many_rows_page_list_in_workspace(gpu):
+    """With many rows the fused call runs the select and the attention as separate kernels,
+    and the select leaves each selected id's page in the workspace's last part (num_rows x
+    topk int32 after the index and attention parts, each 256-byte aligned): the block-table
+    entry of the row's request for a valid id, -1 for an empty slot (5-block rows)."""
+    seq, ql, G, topk = [30_000, 600], [300, 40], 4, 8
+    say("[page list] 340 prefill rows")
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc, prefill=True)
+    R = step.ids.shape[0]
+    mb = wc.layout.max_blocks
+    ws = gpu.index_attend_workspace(step.rows, mb, topk, G, DEV)
+    ws.fill_(0x7F)
+    ids = torch.full((R, topk), -9, dtype=torch.int32, device=DEV)
+    out = torch.empty((R, G, 128), dtype=torch.float32, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gpu.m3s_index_topk_attend(step.cache, wc.q_idx, wc.q, step.bt, mb, step.rows, topk, 0.3, topk_ids=ids,
+                              out=out, workspace=ws, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and torch.equal(ids, step.ids)
+    a256 = lambda n: (n + 255) // 256 * 256
+    off = a256(gpu.m3s_workspace_bytes(gpu.OP_INDEX_TOPK, R, 2, mb, topk, G)) + \
+        a256(gpu.m3s_workspace_bytes(gpu.OP_SPARSE_ATTEND, R, 2, mb, topk, G))
+    assert ws.numel() == off + a256(R * topk * 4)
+    pages = ws[off: off + R * topk * 4].cpu().view(torch.int32).reshape(R, topk).numpy()
+    got = ids.cpu().numpy()
+    bt = step.bt.cpu().numpy()
+    req = step.rows.row_req.cpu().numpy()
+    want = np.where(got >= 0, bt[req[:, None], np.maximum(got, 0)], -1)
+    assert (got == -1).any() and (got >= 0).any()
+    assert np.array_equal(pages, want)
