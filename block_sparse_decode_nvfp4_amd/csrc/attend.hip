@@ -6,8 +6,9 @@
 // the review note that an invalid block id must not wrap onto a valid page.
 //
 // split kernel - workgroup (row, split), 8 waves, two per selected block, each
-//   taking 64 of its tokens (so a split covers 4 of the row's k blocks). Per
-//   wave:
+//   taking 64 of its tokens (so a split covers 4 of the row's k blocks; with
+//   many more split workgroups than fit the GPU at once, each wave takes two
+//   blocks in turn and a split covers 8). Per wave and block:
 //     S^T = K Q^T on fp16 MFMA (K tile of 16 tokens as A, the G <= 16 query
 //       heads as B); K is decoded exactly to fp16 (code * scale).
 //     online softmax in fp32 over the block's causal tokens;
@@ -25,8 +26,10 @@
 
 namespace m3s {
 
-template <int FMT>
-__global__ __launch_bounds__(kWaves * 64) void attend_split_kernel(AttendArgs a) {
+// Two blocks per wave are kept to four waves per SIMD (128 VGPRs), so two
+// workgroups still share a CU.
+template <int FMT, int REPS>
+__global__ __launch_bounds__(kWaves * 64, REPS == 1 ? 1 : 4) void attend_split_kernel(AttendArgs a) {
   __shared__ AttendShared sh;
   int r, sp;
   if (a.xcd_rows) {
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(kWaves * 64) void attend_split_kernel(AttendArgs a)
     r = blockIdx.x / a.nsplit;
     sp = blockIdx.x - r * a.nsplit;
   }
-  attend_split_body<FMT>(a, r, sp, sh, nullptr, nullptr, 0, 0);
+  attend_split_body<FMT, REPS>(a, r, sp, sh, nullptr, nullptr, 0, 0);
 }
 
 // All partials of the row are loaded before any is used (one round trip);
@@ -95,10 +98,17 @@ size_t attend_ws_bytes(int32_t num_rows, int32_t nsplit) {
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)a.num_rows * a.nsplit);
-  if (a.format == 1)
-    hipLaunchKernelGGL(attend_split_kernel<1>, dim3(grid), dim3(kWaves * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attend_split_kernel<2>, dim3(grid), dim3(kWaves * 64), 0, stream, a);
+  if (a.reps == 2) {
+    if (a.format == 1)
+      hipLaunchKernelGGL((attend_split_kernel<1, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attend_split_kernel<2, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
+  } else {
+    if (a.format == 1)
+      hipLaunchKernelGGL((attend_split_kernel<1, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attend_split_kernel<2, 1>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   return launch_attend_combine(a, stream);

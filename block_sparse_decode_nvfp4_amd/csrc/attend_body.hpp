@@ -73,189 +73,222 @@ __device__ __forceinline__ void row_split_of(int b, int nsplit, int num_rows, in
 // lookup), or, when s_ids is given (the select ran in the same workgroup), the
 // ids, their pages and the row's request and length come from the caller (LDS /
 // registers).
-template <int FMT>
+template <int FMT, int REPS = 1>
 __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, int sp, AttendShared& sh,
                                                   const int* s_ids, const int* s_pages, int b_in, int len_in) {
   constexpr int SB = FMT == 1 ? 8 : 4;
   typedef Decode<FMT> Dec;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int n = lane & 15, G = lane >> 4;
-  const int slot = sp * kBlocks + w / kHalves;
   const int half = w % kHalves;  // tokens [64 half, 64 half + 64) of the block
 
-  // ---- which block this wave attends; the row map, the id and the query are
+  // ---- which blocks this wave attends; the row map, the ids and the query are
   // independent loads, issued together
   const int b = s_ids ? b_in : a.row_req[r];
   const int len = s_ids ? len_in : a.row_len[r];
-  const int id = slot < a.topk ? (s_ids ? s_ids[slot] : a.topk_ids[(int64_t)r * a.topk + slot]) : -1;
-  const int pg_sel = (!s_ids && a.sel_pages && slot < a.topk) ? a.sel_pages[(int64_t)r * a.topk + slot] : -1;
+  int id[REPS], pg_sel[REPS];
+#pragma unroll
+  for (int rep = 0; rep < REPS; ++rep) {
+    const int slot = (sp * REPS + rep) * kBlocks + w / kHalves;
+    id[rep] = slot < a.topk ? (s_ids ? s_ids[slot] : a.topk_ids[(int64_t)r * a.topk + slot]) : -1;
+    pg_sel[rep] = (!s_ids && a.sel_pages && slot < a.topk) ? a.sel_pages[(int64_t)r * a.topk + slot] : -1;
+  }
   u32x4 raw[4] = {};
   if (n < a.num_heads) {
     const uint16_t* qp = a.q + (int64_t)r * a.q_row_stride + (int64_t)n * a.q_head_stride + 32 * G;
 #pragma unroll
     for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
   }
-  int page = -1, blk = -1;
-  if (b >= 0 && len > 0 && slot < a.topk) {
-    const int nbr = (len + kPage - 1) / kPage;
-    if (id >= 0) {
-      if (id >= nbr || id >= a.max_blocks) {
-        if (lane == 0) set_status(a.status, kDevBadBlockId);
-      } else {
-        const int pg = s_ids ? s_pages[slot]
-                             : (a.sel_pages ? pg_sel : a.block_table[(int64_t)b * a.bt_stride + id]);
-        if (pg < 0 || pg >= a.num_pages) {
-          if (lane == 0) set_status(a.status, kDevBadPage);
+  int page[REPS], blk[REPS];
+#pragma unroll
+  for (int rep = 0; rep < REPS; ++rep) {
+    const int slot = (sp * REPS + rep) * kBlocks + w / kHalves;
+    page[rep] = -1;
+    blk[rep] = -1;
+    if (b >= 0 && len > 0 && slot < a.topk) {
+      const int nbr = (len + kPage - 1) / kPage;
+      if (id[rep] >= 0) {
+        if (id[rep] >= nbr || id[rep] >= a.max_blocks) {
+          if (lane == 0) set_status(a.status, kDevBadBlockId);
         } else {
-          page = pg;
-          blk = id;
+          const int pg = s_ids ? s_pages[slot]
+                               : (a.sel_pages ? pg_sel[rep] : a.block_table[(int64_t)b * a.bt_stride + id[rep]]);
+          if (pg < 0 || pg >= a.num_pages) {
+            if (lane == 0) set_status(a.status, kDevBadPage);
+          } else {
+            page[rep] = pg;
+            blk[rep] = id[rep];
+          }
         }
       }
     }
   }
-  const bool active = page >= 0;
 
   float m_run = -INFINITY, l_run = 0.f;  // per head n (replicated over G)
   f32x4 o[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (active) {
-    // ---- K and V loads for the whole block (lane: token 16 i + n, dims [32G, 32G + 32))
-    const uint8_t* kp = a.k_data + (int64_t)page * (kPage * kPayload);
-    const uint8_t* vp = a.v_data + (int64_t)page * (kPage * kPayload);
-    const uint8_t* ksp = a.k_scale + (int64_t)page * (kPage * SB);
-    const uint8_t* vsp = a.v_scale + (int64_t)page * (kPage * SB);
-    u32x4 kr[kTiles];
-    uint32_t ks[kTiles];
-    const int t0 = 16 * kTiles * half;  // first token of the wave's tiles
+  // ---- the wave's blocks, one after another (REPS > 1: online softmax across them)
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) kr[i] = *reinterpret_cast<const u32x4*>(kp + (t0 + 16 * i + n) * kPayload + 16 * G);
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      if (FMT == 1) ks[i] = *reinterpret_cast<const uint16_t*>(ksp + (t0 + 16 * i + n) * SB + 2 * G);
-      else ks[i] = ksp[(t0 + 16 * i + n) * SB + G];
-    }
+  for (int rep = 0; rep < REPS; ++rep) {
+    const bool active = page[rep] >= 0;
 
-    // ---- V loads, issued with the K loads (same lane mapping)
-    u32x4 vr[kTiles];
-    uint32_t vs[kTiles];
+    if (active) {
+      // ---- K and V loads for the whole block (lane: token 16 i + n, dims [32G, 32G + 32))
+      const uint8_t* kp = a.k_data + (int64_t)page[rep] * (kPage * kPayload);
+      const uint8_t* vp = a.v_data + (int64_t)page[rep] * (kPage * kPayload);
+      const uint8_t* ksp = a.k_scale + (int64_t)page[rep] * (kPage * SB);
+      const uint8_t* vsp = a.v_scale + (int64_t)page[rep] * (kPage * SB);
+      u32x4 kr[kTiles];
+      uint32_t ks[kTiles];
+      const int t0 = 16 * kTiles * half;  // first token of the wave's tiles
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) vr[i] = *reinterpret_cast<const u32x4*>(vp + (t0 + 16 * i + n) * kPayload + 16 * G);
+      for (int i = 0; i < kTiles; ++i)
+        kr[i] = *reinterpret_cast<const u32x4*>(kp + (t0 + 16 * i + n) * kPayload + 16 * G);
 #pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      if (FMT == 1) vs[i] = *reinterpret_cast<const uint16_t*>(vsp + (t0 + 16 * i + n) * SB + 2 * G);
-      else vs[i] = vsp[(t0 + 16 * i + n) * SB + G];
-    }
-
-    // ---- query heads as the B operand, scaled by 2^P into fp16 range
-    uint32_t mx = 0;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
-    mx = lane_max<1, 64>(mx);
-    int P = 0;
-    if (mx) {
-      const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
-      const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
-      P = 13 - fl;
-      P = P > 64 ? 64 : (P < -64 ? -64 : P);
-    }
-    f16x8 qop[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
-        qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
+      for (int i = 0; i < kTiles; ++i) {
+        if (FMT == 1) ks[i] = *reinterpret_cast<const uint16_t*>(ksp + (t0 + 16 * i + n) * SB + 2 * G);
+        else ks[i] = ksp[(t0 + 16 * i + n) * SB + G];
       }
-    // logits in log2 units: x = S' * sm_scale * log2(e) * 2^-P
-    const float c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
 
-    // ---- S^T tiles: st[i][v] = logit of token t0 + 16 i + 4 G + v for head n
-    f32x4 st[kTiles];
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      typename Dec::scale_t s0, s1;
-      if (FMT == 1) { s0 = Dec::scale(ks[i] & 0xFFu); s1 = Dec::scale(ks[i] >> 8); }
-      else { s0 = s1 = Dec::scale(ks[i]); }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma_f16(Dec::run(kr[i][s], s < 2 ? s0 : s1), qop[s], acc);
-      st[i] = acc * c;
-    }
-    const int tok_base = blk * kPage + t0;
-    if (tok_base + 16 * kTiles > len) {
+      // ---- V loads, issued with the K loads (same lane mapping)
+      u32x4 vr[kTiles];
+      uint32_t vs[kTiles];
 #pragma unroll
       for (int i = 0; i < kTiles; ++i)
+        vr[i] = *reinterpret_cast<const u32x4*>(vp + (t0 + 16 * i + n) * kPayload + 16 * G);
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          if (tok_base + 16 * i + 4 * G + v >= len) st[i][v] = -INFINITY;
-    }
-    float mx_l = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kTiles; ++i) mx_l = fmaxf(mx_l, fmaxf(fmaxf(st[i][0], st[i][1]), fmaxf(st[i][2], st[i][3])));
-    mx_l = lane_fmax<16, 64>(mx_l);
-    // a wave's 64 tokens can all lie past the row's length: it then stays empty
-    if (tok_base < len) {
-      m_run = mx_l;  // finite: the wave's tokens include a causal one
-      float lsum = 0.f;
-#pragma unroll
-      for (int i = 0; i < kTiles; ++i)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = __builtin_amdgcn_exp2f(st[i][v] - mx_l);
-          st[i][v] = p;
-          lsum += p;
-        }
-      lsum = lane_sum<16, 64>(lsum);
-      l_run = lsum;
+      for (int i = 0; i < kTiles; ++i) {
+        if (FMT == 1) vs[i] = *reinterpret_cast<const uint16_t*>(vsp + (t0 + 16 * i + n) * SB + 2 * G);
+        else vs[i] = vsp[(t0 + 16 * i + n) * SB + G];
+      }
 
-      // ---- O += P V, kVChunk tokens staged per step, 32 per MFMA
-      _Float16(*vb)[kVRow] = sh.v[w];
+      // ---- query heads as the B operand, scaled by 2^P into fp16 range
+      uint32_t mx = 0;
 #pragma unroll
-      for (int cidx = 0; cidx < 16 * kTiles / kVChunk; ++cidx) {
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int h4 = 0; h4 < kVChunk / 16; ++h4) {
-          const int i = (kVChunk / 16) * cidx + h4;
-          typename Dec::scale_t s0, s1;
-          if (FMT == 1) { s0 = Dec::scale(vs[i] & 0xFFu); s1 = Dec::scale(vs[i] >> 8); }
-          else { s0 = s1 = Dec::scale(vs[i]); }
-          _Float16* dst = &vb[16 * h4 + n][32 * G];
+        for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
+      mx = lane_max<1, 64>(mx);
+      int P = 0;
+      if (mx) {
+        const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
+        const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
+        P = 13 - fl;
+        P = P > 64 ? 64 : (P < -64 ? -64 : P);
+      }
+      f16x8 qop[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            *reinterpret_cast<f16x8*>(dst + 8 * s) = Dec::run(vr[i][s], s < 2 ? s0 : s1);
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
+          qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // logits in log2 units: x = S' * sm_scale * log2(e) * 2^-P
+      const float c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
+
+      // ---- S^T tiles: st[i][v] = logit of token t0 + 16 i + 4 G + v for head n
+      f32x4 st[kTiles];
 #pragma unroll
-        for (int ks = 0; ks < kVChunk / 32; ++ks) {
-          const int i0 = (kVChunk / 16) * cidx + 2 * ks;
-          // A operand: head n, tokens {4G..4G+3} of tile i0 then of tile i0 + 1
-          f16x8 pa;
+      for (int i = 0; i < kTiles; ++i) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        typename Dec::scale_t s0, s1;
+        if (FMT == 1) { s0 = Dec::scale(ks[i] & 0xFFu); s1 = Dec::scale(ks[i] >> 8); }
+        else { s0 = s1 = Dec::scale(ks[i]); }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma_f16(Dec::run(kr[i][s], s < 2 ? s0 : s1), qop[s], acc);
+        st[i] = acc * c;
+      }
+      const int tok_base = blk[rep] * kPage + t0;
+      if (tok_base + 16 * kTiles > len) {
+#pragma unroll
+        for (int i = 0; i < kTiles; ++i)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            if (tok_base + 16 * i + 4 * G + v >= len) st[i][v] = -INFINITY;
+      }
+      float mx_l = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kTiles; ++i) mx_l = fmaxf(mx_l, fmaxf(fmaxf(st[i][0], st[i][1]), fmaxf(st[i][2], st[i][3])));
+      mx_l = lane_fmax<16, 64>(mx_l);
+      // a wave's 64 tokens can all lie past the row's length: it then stays empty
+      if (tok_base < len) {
+        // mx_l is finite: the wave's tokens include a causal one. Over several
+        // blocks the running sum and O are rescaled to the new running max.
+        const float m_new = REPS == 1 ? mx_l : fmaxf(m_run, mx_l);
+        float lsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < kTiles; ++i)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            pa[v] = (_Float16)st[i0][v];
-            pa[4 + v] = (_Float16)st[i0 + 1][v];
+            const float p = __builtin_amdgcn_exp2f(st[i][v] - m_new);
+            st[i][v] = p;
+            lsum += p;
           }
-          // B operand for N tile t: V[those 8 tokens][16 t + n]; lane n of a 16-lane
-          // group points at token (4G + n / 4), dims 16 t + 4 (n % 4) .. + 3.
-          const int r0 = 32 * ks + 4 * G + (n >> 2);
+        lsum = lane_sum<16, 64>(lsum);
+        if constexpr (REPS == 1) {
+          l_run = lsum;
+        } else {
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // head n; 0 while m_run is -inf
+          l_run = l_run * alpha + lsum;
+          // o[t][v] is head 4G + v: its factor comes from lane 4G + v (n = 4G + v)
+          float av[4];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const f16x4 lo = lds_tr16(&vb[r0][16 * t + 4 * (n & 3)]);
-            const f16x4 hi = lds_tr16(&vb[r0 + 16][16 * t + 4 * (n & 3)]);
-            f16x8 bv;
-            bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
-            bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
-            o[t] = mfma_f16(pa, bv, o[t]);
-          }
+          for (int v = 0; v < 4; ++v) av[v] = __shfl(alpha, 4 * G + v, 64);
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[t][v] *= av[v];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        m_run = m_new;
+
+        // ---- O += P V, kVChunk tokens staged per step, 32 per MFMA
+        _Float16(*vb)[kVRow] = sh.v[w];
+#pragma unroll
+        for (int cidx = 0; cidx < 16 * kTiles / kVChunk; ++cidx) {
+#pragma unroll
+          for (int h4 = 0; h4 < kVChunk / 16; ++h4) {
+            const int i = (kVChunk / 16) * cidx + h4;
+            typename Dec::scale_t s0, s1;
+            if (FMT == 1) { s0 = Dec::scale(vs[i] & 0xFFu); s1 = Dec::scale(vs[i] >> 8); }
+            else { s0 = s1 = Dec::scale(vs[i]); }
+            _Float16* dst = &vb[16 * h4 + n][32 * G];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              *reinterpret_cast<f16x8*>(dst + 8 * s) = Dec::run(vr[i][s], s < 2 ? s0 : s1);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+#pragma unroll
+          for (int ks = 0; ks < kVChunk / 32; ++ks) {
+            const int i0 = (kVChunk / 16) * cidx + 2 * ks;
+            // A operand: head n, tokens {4G..4G+3} of tile i0 then of tile i0 + 1
+            f16x8 pa;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              pa[v] = (_Float16)st[i0][v];
+              pa[4 + v] = (_Float16)st[i0 + 1][v];
+            }
+            // B operand for N tile t: V[those 8 tokens][16 t + n]; lane n of a 16-lane
+            // group points at token (4G + n / 4), dims 16 t + 4 (n % 4) .. + 3.
+            const int r0 = 32 * ks + 4 * G + (n >> 2);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const f16x4 lo = lds_tr16(&vb[r0][16 * t + 4 * (n & 3)]);
+              const f16x4 hi = lds_tr16(&vb[r0 + 16][16 * t + 4 * (n & 3)]);
+              f16x8 bv;
+              bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
+              bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
+              o[t] = mfma_f16(pa, bv, o[t]);
+            }
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
       }
     }
   }

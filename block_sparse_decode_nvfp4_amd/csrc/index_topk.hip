@@ -1138,7 +1138,7 @@ hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, h
   hipError_t e = launch_scan(ia, stream);
   if (e != hipSuccess) return e;
   const int64_t wgs = (int64_t)ia.num_rows * aa.nsplit;
-  if (wgs > 2 * (int64_t)ia.scan_grid) {
+  if (wgs > 2 * (int64_t)ia.scan_grid || aa.reps != 1) {
     // Many rows (prefill): every split's workgroup would repeat its row's select,
     // which only pays while the launch is latency-bound (measured at a 4096-row
     // chunk: twice the time of the separate kernels). Same results either way.
