@@ -377,11 +377,11 @@ m3s_status attend_args(AttendArgs& a, const m3s_cache* cache, const uint16_t* q,
   // L2; measured faster while every split workgroup is resident at once (64 rows:
   // 14.9 -> 14.1 us), slightly slower with several rounds of workgroups (384 rows).
   a.xcd_rows = rows->num_rows > 0 && (int64_t)rows->num_rows * nsplit <= 2 * (int64_t)scan_grid() ? 1 : 0;
-  // With more than four rounds of split workgroups, each wave attends two blocks
+  // With more than two rounds of split workgroups, each wave attends two blocks
   // in turn (online softmax across them): half the splits, so half the partials
   // written and combined. The workspace stays sized for the larger split count.
   a.reps = 1;
-  if (nsplit > 1 && rows->num_rows > 0 && (int64_t)rows->num_rows * nsplit > 8 * (int64_t)scan_grid()) {
+  if (nsplit > 1 && rows->num_rows > 0 && (int64_t)rows->num_rows * nsplit > 4 * (int64_t)scan_grid()) {
     a.reps = 2;
     a.nsplit = (nsplit + 1) / 2;
   }
