@@ -24,7 +24,7 @@ cache", Design / Write path; ATOM PR "NVFP4 sparse KV", Summary):
          64 B payload + 4 B scales = 68 B. The pages give no scale rule; the
          OCP MX v1.0 rule is taken: X = 2^(floor(log2 amax) - 2), clamped to
          the E8M0 range, codes = RNE-saturating e2m1 of x / X.
-Packing (reading of "even/odd row loads"): byte j of the payload holds
+Packing (reading of the kernels' loads of even and odd elements): byte j of the payload holds
 element 2j in its low nibble and element 2j+1 in its high nibble; scale
 byte g covers elements [16 g, 16 g + 16) (NVFP4) or [32 g, 32 g + 32) (MXFP4).
 Sign bit of a code = (x < 0): -0.0 gives 0x0, a small negative that rounds to

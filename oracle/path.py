@@ -15,14 +15,14 @@ Each function follows the pages:
     (reading of the index score; the pages print no formula).
   * topk_blocks: the k best blocks; equal scores go to the lower block id by
     default (or to the higher id, the rule of the ATOM review notes on
-    ``_pack_score_key``); ids are emitted ascending, padded with -1 (the fused
-    top-k "emits ascending ids"). Forced initial / local blocks (vLLM PR
+    ``_pack_score_key``); ids are emitted ascending, padded with -1 (the review
+    notes state that the fused top-k writes its ids in ascending order). Forced initial / local blocks (vLLM PR
     "MXFP4 KV + indexer cache for MiniMax-M3.1", Design; ATOM review notes on
     init_blocks + local_blocks > topk) rank above every scored block.
   * attend_row: softmax attention of the row's G query heads over the tokens
     of the selected blocks that are causal for the row, with the dequantized
-    K/V (ATOM PR "NVFP4 sparse KV", Tests: "against the dequantized
-    reference").
+    K/V (ATOM PR "NVFP4 sparse KV", Tests: the kernel is checked against
+    attention computed on the dequantized cache).
 
 Exactness of the scores: every dequantized NVFP4 key element has at most 6
 significant bits and a bf16 query element 8, so each product is exact in
@@ -68,7 +68,8 @@ def prefill_rows(cu_q, seq_lens, num_rows):
     """Prefill rows: every query token of a request's chunk is a row and sees the request's
     prefix plus the chunk up to itself, the same map as ``decode_rows`` with no bound on a
     request's row count (the pages' prefill_rows, ATOM PR "[MiniMax-M3.1] FP4 index cache
-    and NVFP4 sparse KV cache", Design: Row maps; "decode_rows / prefill_rows match torch")."""
+    and NVFP4 sparse KV cache", Design: Row maps, which reports both device row maps agreeing
+    with the torch mapping they replace)."""
     return decode_rows(cu_q, seq_lens, num_rows)
 
 
@@ -173,14 +174,6 @@ def topk_blocks(scores: np.ndarray, k: int, tie_high: bool = False, init_blocks:
     out = np.full(k, -1, dtype=np.int32)
     out[: len(sel)] = sel
     return out
-
-
-def cutoff_margin(scores: np.ndarray, k: int) -> float:
-    """S_k - S_{k+1} of the sorted scores (inf when every block is selected)."""
-    if len(scores) <= k:
-        return math.inf
-    s = np.sort(np.asarray(scores))[::-1]
-    return float(s[k - 1] - s[k])
 
 
 def selected_tokens(ids, row_len: int) -> np.ndarray:
