@@ -2,6 +2,8 @@
 same step through the oracle, on the same seeded inputs (workloads)."""
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 import sys
 from dataclasses import dataclass
 
@@ -80,37 +82,59 @@ def _m3s_cache(m3s, fmt, num_pages, dev):
 
 
 def oracle_requests(step: GpuStep, fmt, topk, sm_scale, requests, tie_high=False, q_idx_bits=None,
-                    init_blocks=0, local_blocks=0):
-    """Oracle ids / outputs for the rows of `requests` (planes quantized by the oracle itself)."""
+                    init_blocks=0, local_blocks=0, threads=None):
+    """Oracle ids / outputs for the rows of `requests` (planes quantized by the oracle itself).
+
+    The oracle's functions run unchanged; independent requests (and rows) run in a thread
+    pool, since the numpy work releases the GIL."""
     case = step.case
     lay = case.layout
     R = step.ids.shape[0]
     qi_bits = W.bf16_bits(case.q_idx) if q_idx_bits is None else q_idx_bits
     q_bits = W.bf16_bits(case.q)
-    want_ids = {}
-    want_out = {}
     row_req, row_len = P.decode_rows(lay.cu_q, lay.seq_lens, R)
     qi = F.bf16_to_f64(qi_bits)
     qm = F.bf16_to_f64(q_bits)
-    for b in requests:
+    requests = list(requests)
+    workers = threads or min(16, max(1, len(os.sched_getaffinity(0))))
+    host = {}
+    kidx = {}
+    want_ids = {}
+    want_out = {}
+
+    def quant(b):
+        kidx[b] = F.dequantize(fmt, *F.quantize(fmt, host[b]["idx"]))
+
+    def select(r):
+        b = int(row_req[r])
+        s = P.block_scores(qi[r], kidx[b], int(row_len[r]))
+        want_ids[r] = P.topk_blocks(s, topk, tie_high, init_blocks, local_blocks)
+
+    def attend(b):
         n = int(lay.seq_lens[b])
-        lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
-        sl = slice(lo, hi)
-        kidx = F.dequantize(fmt, *F.quantize(fmt, W.bf16_bits(case.idx[sl])))
         rows = range(int(lay.cu_q[b]), int(lay.cu_q[b + 1]))
-        need = set()
-        for r in rows:
-            s = P.block_scores(qi[r], kidx, int(row_len[r]))
-            want_ids[r] = P.topk_blocks(s, topk, tie_high, init_blocks, local_blocks)
-            need |= {int(j) for j in want_ids[r] if j >= 0}
+        need = sorted({int(j) for r in rows for j in want_ids[r] if j >= 0})
         kh = np.zeros((n, 128))
         vh = np.zeros((n, 128))
-        for j in sorted(need):
-            t = slice(lo + j * 128, lo + min(n, (j + 1) * 128))
-            kh[j * 128: j * 128 + (t.stop - t.start)] = F.dequantize(fmt, *F.quantize(fmt, W.bf16_bits(case.k[t])))
-            vh[j * 128: j * 128 + (t.stop - t.start)] = F.dequantize(fmt, *F.quantize(fmt, W.bf16_bits(case.v[t])))
+        for j in need:
+            t = slice(j * 128, min(n, (j + 1) * 128))
+            kh[t] = F.dequantize(fmt, *F.quantize(fmt, host[b]["k"][t]))
+            vh[t] = F.dequantize(fmt, *F.quantize(fmt, host[b]["v"][t]))
         for r in rows:
             want_out[r] = P.attend_row(qm[r], kh, vh, want_ids[r], int(row_len[r]), sm_scale)
+
+    with cf.ThreadPoolExecutor(workers) as ex:
+        # batches of requests bound the host rows and dequantized planes held at once
+        for i in range(0, len(requests), workers):
+            batch = requests[i: i + workers]
+            for b in batch:   # host copies of the request's rows (device tensors), serially
+                lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
+                host[b] = {n: W.bf16_bits(getattr(case, n)[lo:hi]) for n in ("idx", "k", "v")}
+            list(ex.map(quant, batch))
+            list(ex.map(select, [r for b in batch for r in range(int(lay.cu_q[b]), int(lay.cu_q[b + 1]))]))
+            kidx.clear()
+            list(ex.map(attend, batch))
+            host.clear()
     return want_ids, want_out, row_req, row_len
 
 

@@ -71,20 +71,36 @@ def test_fused_equals_separate_calls(gpu, case):
     assert torch.equal(out, step.out)
 
 
-def test_fused_against_oracle(gpu):
-    """Ids exact and attention within 5e-3 of the oracle, directly."""
-    seq, ql, G, topk = [40_000, 2000, 9000], 8, 8, 16
+ORACLE_CASES = [
+    # fmt, seq_lens, q_len, G, topk
+    ("nvfp4", [40_000, 2000, 9000], 8, 8, 16),
+    ("nvfp4", [40_000, 2000, 9000], 8, 12, 16),         # G not a power of two
+    ("mxfp4", [30_000, 700], 4, 3, 16),                 # G not a power of two
+    ("nvfp4", [500_000], 2, 2, 16),                     # 3907 blocks: 16 per thread
+    ("mxfp4", [1_000_000], 2, 2, 16),                   # 7813 blocks: 32 per thread
+]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("case", ORACLE_CASES, ids=[f"{c[0]}-G{c[3]}-{max(c[1])}" for c in ORACLE_CASES])
+def test_fused_against_oracle(gpu, case):
+    """Ids exact and attention within 5e-3 of the oracle, directly, on every row."""
+    fmt, seq, ql, G, topk = case
+    say(f"[fused vs oracle] {case}")
     wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=ql, G=G)
-    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, sm_scale=0.3, case=wc)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, fmt=fmt, sm_scale=0.3, case=wc)
+    assert step.status == 0, hex(step.status)
     ids, out, st = _fused(gpu, step, topk, 0.3)
     assert st == 0
-    want_ids, want_out, _, _ = oracle_requests(step, "nvfp4", topk, 0.3, range(len(seq)))
+    want_ids, want_out, _, _ = oracle_requests(step, fmt, topk, 0.3, range(len(seq)))
+    assert len(want_ids) == ids.shape[0]
     got = ids.cpu().numpy()
     o = out.cpu().double().numpy()
     worst = 0.0
     for r, w in want_ids.items():
         assert got[r].tolist() == w.tolist(), r
         worst = max(worst, max_rel_err(o[r], want_out[r]))
+    say(f"[fused vs oracle] max rel err {worst:.2e}")
     assert worst <= 5e-3, worst
 
 
