@@ -9,12 +9,13 @@
 //   taking 64 of its tokens (so a split covers 4 of the row's k blocks; with
 //   many more split workgroups than fit the GPU at once, each wave takes two
 //   blocks in turn and a split covers 8). Per wave and block:
-//     S^T = K Q^T on fp16 MFMA (K tile of 16 tokens as A, the G <= 16 query
-//       heads as B); K is decoded exactly to fp16 (code * scale).
+//     S^T = K Q^T on 16-bit MFMA (K tile of 16 tokens as A, the G <= 16
+//       query heads as B); K is decoded exactly (NVFP4 to fp16, MXFP4 to
+//       bf16).
 //     online softmax in fp32 over the block's causal tokens;
-//     O += P V on fp16 MFMA: P comes straight out of the S^T registers as
-//       the A operand; V is decoded to fp16 into LDS token-major and read
-//       back transposed with ds_read_b64_tr_b16 as the B operand.
+//     O += P V on 16-bit MFMA: P comes out of the S^T registers as the A
+//       operand; V is decoded into LDS token-major and read back transposed
+//       with ds_read_b64_tr_b16 as the B operand.
 //   The 8 waves merge through LDS and write one (m, l, O) partial per head.
 // combine kernel - one workgroup per row merges the splits:
 //   out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s (log2 domain).
@@ -82,8 +83,16 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   f32x4* dst = reinterpret_cast<f32x4*>(a.out + ((int64_t)r * a.num_heads + hh) * kDim + d0);
-  dst[0] = acc0 * inv;
-  dst[1] = acc1 * inv;
+  bool bad = false;
+  f32x4 o0, o1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o0[e] = finite_or_zero(acc0[e] * inv, bad);
+    o1[e] = finite_or_zero(acc1[e] * inv, bad);
+  }
+  dst[0] = o0;
+  dst[1] = o1;
+  if (bad) set_status(a.status, kDevRange);
 }
 
 int32_t attend_nsplit(int32_t topk) { return (topk + kBlocks - 1) / kBlocks; }

@@ -2,12 +2,19 @@
 // m3s_sparse_attend split kernel and the fused top-k + attention kernel.
 // Workgroup (row, split): 8 waves, two per selected block, each taking 64 of
 // its tokens (so a split covers 4 of the row's k blocks). Per wave:
-//   S^T = K Q^T on fp16 MFMA (K tile of 16 tokens as A, the G <= 16 query
-//     heads as B); K is decoded exactly to fp16 (code * scale).
+//   S^T = K Q^T on 16-bit MFMA (K tile of 16 tokens as A, the G <= 16 query
+//     heads as B); K is decoded exactly: NVFP4 to fp16 (the query scaled by a
+//     power of two into fp16 range), MXFP4 to bf16 (the bf16 query as is),
+//     since only bf16 holds code * 2^(b - 127) for every E8M0 byte.
 //   online softmax in fp32 over the block's causal tokens;
-//   O += P V on fp16 MFMA: P comes straight out of the S^T registers as the A
-//     operand; V is decoded to fp16 into LDS token-major and read back
-//     transposed with ds_read_b64_tr_b16 as the B operand.
+//   O += P V on 16-bit MFMA: P comes out of the S^T registers as the A
+//     operand (NVFP4: one fp16 term; MXFP4: P = hi + lo, two bf16 terms and
+//     two MFMAs, so P keeps 16 significant bits); V is decoded into LDS
+//     token-major and read back transposed with ds_read_b64_tr_b16 as the B
+//     operand.
+// An output element that is not finite in fp32 (a logit or sum beyond the
+// fp32 range, e.g. MXFP4 scale bytes 253 and 254, which no store writes) is
+// written as 0 and sets the range status bit.
 // The 8 waves merge through LDS and write one (m, l, O) partial per head (or,
 // with a single split, the normalized output).
 #pragma once
@@ -39,10 +46,27 @@ struct AttendShared {
   };
 };
 
-__device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+__device__ __forceinline__ s16x4 lds_tr16(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) void*)p));
-  return __builtin_bit_cast(f16x4, r);
+}
+
+// B operand of 8 16-bit values from two transposing reads (bits as read).
+template <typename OP>
+__device__ __forceinline__ OP tr16_pair(s16x4 lo, s16x4 hi) {
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(OP, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) { return mfma_f16(a, b, c); }
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) { return mfma_bf16(a, b, c); }
+
+// An output value, or 0 with the range flag set when it is not finite.
+__device__ __forceinline__ float finite_or_zero(float v, bool& bad) {
+  const bool ok = __builtin_isfinite(v);
+  bad |= !ok;
+  return ok ? v : 0.f;
 }
 
 // Workgroup b of a (row, split) grid -> its row and split, with all splits of a
@@ -164,30 +188,38 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
         else vs[i] = vsp[(t0 + 16 * i + n) * SB + G];
       }
 
-      // ---- query heads as the B operand, scaled by 2^P into fp16 range
-      uint32_t mx = 0;
+      // ---- query heads as the B operand: NVFP4 scaled by 2^P into fp16 range; MXFP4
+      // the bf16 values as they are
+      typedef typename Dec::op_t op_t;
+      op_t qop[4];
+      float c;  // logits in log2 units: x = S' * c
+      if constexpr (FMT == 1) {
+        uint32_t mx = 0;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
-      mx = lane_max<1, 64>(mx);
-      int P = 0;
-      if (mx) {
-        const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
-        const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
-        P = 13 - fl;
-        P = P > 64 ? 64 : (P < -64 ? -64 : P);
-      }
-      f16x8 qop[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
-          qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
+          for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
+        mx = lane_max<1, 64>(mx);
+        int P = 0;
+        if (mx) {
+          const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
+          const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
+          P = 13 - fl;
+          P = P > 64 ? 64 : (P < -64 ? -64 : P);
         }
-      // logits in log2 units: x = S' * sm_scale * log2(e) * 2^-P
-      const float c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
+            qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
+          }
+        c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8, raw[s]);
+        c = a.sm_scale * 1.4426950408889634f;
+      }
 
       // ---- S^T tiles: st[i][v] = logit of token t0 + 16 i + 4 G + v for head n
       f32x4 st[kTiles];
@@ -198,7 +230,7 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
         if (FMT == 1) { s0 = Dec::scale(ks[i] & 0xFFu); s1 = Dec::scale(ks[i] >> 8); }
         else { s0 = s1 = Dec::scale(ks[i]); }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma_f16(Dec::run(kr[i][s], s < 2 ? s0 : s1), qop[s], acc);
+        for (int s = 0; s < 4; ++s) acc = mfma16(Dec::run(kr[i][s], s < 2 ? s0 : s1), qop[s], acc);
         st[i] = acc * c;
       }
       const int tok_base = blk[rep] * kPage + t0;
@@ -257,7 +289,7 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
             _Float16* dst = &vb[16 * h4 + n][32 * G];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-              *reinterpret_cast<f16x8*>(dst + 8 * s) = Dec::run(vr[i][s], s < 2 ? s0 : s1);
+              *reinterpret_cast<op_t*>(dst + 8 * s) = Dec::run(vr[i][s], s < 2 ? s0 : s1);
           }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
           __builtin_amdgcn_wave_barrier();
@@ -266,23 +298,41 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
           for (int ks = 0; ks < kVChunk / 32; ++ks) {
             const int i0 = (kVChunk / 16) * cidx + 2 * ks;
             // A operand: head n, tokens {4G..4G+3} of tile i0 then of tile i0 + 1
-            f16x8 pa;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              pa[v] = (_Float16)st[i0][v];
-              pa[4 + v] = (_Float16)st[i0 + 1][v];
-            }
             // B operand for N tile t: V[those 8 tokens][16 t + n]; lane n of a 16-lane
             // group points at token (4G + n / 4), dims 16 t + 4 (n % 4) .. + 3.
             const int r0 = 32 * ks + 4 * G + (n >> 2);
+            if constexpr (FMT == 1) {
+              f16x8 pa;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const f16x4 lo = lds_tr16(&vb[r0][16 * t + 4 * (n & 3)]);
-              const f16x4 hi = lds_tr16(&vb[r0 + 16][16 * t + 4 * (n & 3)]);
-              f16x8 bv;
-              bv[0] = lo[0]; bv[1] = lo[1]; bv[2] = lo[2]; bv[3] = lo[3];
-              bv[4] = hi[0]; bv[5] = hi[1]; bv[6] = hi[2]; bv[7] = hi[3];
-              o[t] = mfma_f16(pa, bv, o[t]);
+              for (int v = 0; v < 4; ++v) {
+                pa[v] = (_Float16)st[i0][v];
+                pa[4 + v] = (_Float16)st[i0 + 1][v];
+              }
+#pragma unroll
+              for (int t = 0; t < 8; ++t) {
+                const f16x8 bv = tr16_pair<f16x8>(lds_tr16(&vb[r0][16 * t + 4 * (n & 3)]),
+                                                  lds_tr16(&vb[r0 + 16][16 * t + 4 * (n & 3)]));
+                o[t] = mfma_f16(pa, bv, o[t]);
+              }
+            } else {
+              // P = hi + lo in bf16 (the remainder is exact in fp32): 16 significant bits
+              bf16x8 ph, pl;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                const float p0 = st[i0][v], p1 = st[i0 + 1][v];
+                const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+                ph[v] = h0;
+                ph[4 + v] = h1;
+                pl[v] = (__bf16)(p0 - (float)h0);
+                pl[4 + v] = (__bf16)(p1 - (float)h1);
+              }
+#pragma unroll
+              for (int t = 0; t < 8; ++t) {
+                const bf16x8 bv = tr16_pair<bf16x8>(lds_tr16(&vb[r0][16 * t + 4 * (n & 3)]),
+                                                    lds_tr16(&vb[r0 + 16][16 * t + 4 * (n & 3)]));
+                o[t] = mfma_bf16(ph, bv, o[t]);
+                o[t] = mfma_bf16(pl, bv, o[t]);
+              }
             }
           }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -330,8 +380,10 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
     if (a.nsplit == 1) {
       const float inv = L > 0.f ? 1.0f / L : 0.f;
       float* dst = a.out + ((int64_t)r * a.num_heads + hh) * kDim + d0;
+      bool bad = false;
 #pragma unroll
-      for (int e = 0; e < kOut; ++e) dst[e] = acc[e] * inv;
+      for (int e = 0; e < kOut; ++e) dst[e] = finite_or_zero(acc[e] * inv, bad);
+      if (bad) set_status(a.status, kDevRange);
     } else {
       float* dst = a.part_o + (((int64_t)r * a.nsplit + sp) * 16 + hh) * kDim + d0;
 #pragma unroll

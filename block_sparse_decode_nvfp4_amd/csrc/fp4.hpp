@@ -60,16 +60,19 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16_unscaled(uint32_t d) {
   return r;
 }
 
-// 8 codes times a power-of-two scale `p2` (E8M0), exact.
-__device__ __forceinline__ f16x8 fp4x8_to_f16_pow2(uint32_t d, float p2) {
-  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 0);
-  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 1);
-  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 2);
-  f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, p2, 3);
-  f16x8 r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = e[0]; r[7] = e[1];
-  return r;
+// 8 codes times a power-of-two scale `p2` (an E8M0 byte as fp32: its exponent field is the
+// byte), as bf16. bf16 has the fp32 exponent range, so code * 2^(b - 127) is exact for
+// every scale byte a store writes (0 .. 252: at most 2 significant bits, magnitudes from
+// 2^-128 to 1.5 * 2^127); 253 and 254 overflow to infinity. The conversion's handling of
+// every code x every byte, subnormal results included, was checked on MI355X.
+// The packed results are kept as raw dwords: extracting the bf16 elements of the
+// builtin's bf16x2 result compiles to a permute that duplicates the low half.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16_pow2(uint32_t d, float p2) {
+  const u32x4 r = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, p2, 0)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, p2, 1)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, p2, 2)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, p2, 3))};
+  return __builtin_bit_cast(bf16x8, r);
 }
 
 // E4M3FN scale byte -> the same value in fp16 (exact: 2^-9 .. 448 are fp16 normals).
@@ -82,19 +85,25 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16_e4m3(uint32_t d, _Float16 s) {
   return r * sv;
 }
 
+// K / V decode of the attention. NVFP4 decodes to fp16 (code * E4M3 scale lies in
+// [2^-10, 2688]: exact in fp16, whose 11-bit significand also keeps P to 2^-12); MXFP4
+// decodes to bf16, the one 16-bit type whose range holds code * 2^(b - 127) for every
+// E8M0 byte. op_t is the MFMA operand of 8 decoded elements.
 template <int FMT>
 struct Decode;
 template <>
 struct Decode<1> {  // NVFP4: scale byte is E4M3FN
   typedef _Float16 scale_t;
+  typedef f16x8 op_t;
   static __device__ __forceinline__ scale_t scale(uint32_t byte) { return e4m3_to_f16(byte); }
-  static __device__ __forceinline__ f16x8 run(uint32_t d, scale_t s) { return fp4x8_to_f16_e4m3(d, s); }
+  static __device__ __forceinline__ op_t run(uint32_t d, scale_t s) { return fp4x8_to_f16_e4m3(d, s); }
 };
 template <>
 struct Decode<2> {  // MXFP4: scale byte is E8M0
   typedef float scale_t;
+  typedef bf16x8 op_t;
   static __device__ __forceinline__ scale_t scale(uint32_t byte) { return e8m0_to_f32(byte); }
-  static __device__ __forceinline__ f16x8 run(uint32_t d, scale_t s) { return fp4x8_to_f16_pow2(d, s); }
+  static __device__ __forceinline__ op_t run(uint32_t d, scale_t s) { return fp4x8_to_bf16_pow2(d, s); }
 };
 
 // Scale of the 16-element (NVFP4) or 32-element (MXFP4) group as fp32.

@@ -18,6 +18,7 @@ enum : uint32_t {
   kDevInexact = 1u << 5,
   kDevBandOverflow = 1u << 6,
   kDevBadPosition = 1u << 7,
+  kDevRange = 1u << 8,
 };
 
 constexpr int kMaxBlocks = 8192;   // causal blocks per request

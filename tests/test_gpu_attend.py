@@ -36,7 +36,7 @@ def _oracle_ids_matrix(want_ids, R, k):
 
 
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-@pytest.mark.parametrize("G,topk", [(1, 1), (4, 4), (16, 5), (16, 16), (2, 64)])
+@pytest.mark.parametrize("G,topk", [(1, 1), (4, 4), (16, 5), (16, 16), (2, 64), (3, 16), (12, 7)])
 def test_attend_small_ragged(gpu, fmt, G, topk):
     seq = [2048, 5000, 300, 129, 128, 127, 17, 9000]
     step = run_gpu_step(gpu, CFG0, DEV, seq_lens=seq, q_len=3, G=G, topk=topk, fmt=fmt, sm_scale=0.37)
@@ -121,3 +121,120 @@ def test_attend_workspace_reuse(gpu, topk):
                                     step.case.cfg.sm_scale, workspace=ws)
         torch.cuda.synchronize()
         assert torch.equal(out, step.out), rep
+
+
+def _many_row_case(topk, G, seed_shift=0):
+    """Enough short requests of 8 rows that rows x splits exceed four times the CU count:
+    the attention's split kernel then takes two blocks per wave (online softmax across
+    them) and half the splits."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nsplit = (topk + 3) // 4
+    rows_needed = 4 * cus // nsplit + 1
+    lens = [300, 2048, 5000, 129, 9000, 700, 3333, 1280]
+    nreq = (rows_needed + 7) // 8 + 1
+    seq = [lens[(i + seed_shift) % len(lens)] + 17 * i for i in range(nreq)]
+    return W.make_case(CFG0, DEV, seq_lens=seq, q_len=8, G=G), nsplit, cus
+
+
+@pytest.mark.parametrize("topk", [5, 12, 16, 20, 64])
+def test_attend_two_blocks_per_wave(gpu, topk):
+    """Many rows (two blocks per attention wave) against the oracle, including top-k values
+    whose last split leaves block slots empty (5, 12, 20) and a 16-split top-k with its
+    combine (64)."""
+    case, nsplit, cus = _many_row_case(topk, 16)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, case=case, sm_scale=0.37)
+    R = step.rows.num_rows
+    assert R * nsplit > 4 * cus
+    assert step.status == 0
+    ids, outs, _, _ = oracle_requests(step, "nvfp4", topk, 0.37, range(len(case.layout.seq_lens)))
+    got, st = _attend(gpu, step, _oracle_ids_matrix(ids, R, topk), 0.37)
+    assert st == 0
+    worst = max(max_rel_err(got[r], want) for r, want in outs.items())
+    assert worst <= TOL, worst
+
+
+def test_attend_two_blocks_per_wave_flags_and_wide_queries(gpu):
+    """Two blocks per wave with invalid ids (past the row's blocks, past max_blocks), a
+    block-table entry outside the cache, and queries spanning a wide range with a sharp
+    softmax: invalid blocks are skipped and flagged, and the rest matches the oracle over
+    the valid blocks."""
+    topk = 16
+    case, nsplit, cus = _many_row_case(topk, 16, seed_shift=3)
+    case.q[0::5, :8] *= 64
+    case.q[1::7, 8:] *= 2.0 ** -20
+    step = run_gpu_step(gpu, CFG0, DEV, topk=topk, case=case, sm_scale=2.0)
+    R = step.rows.num_rows
+    assert R * nsplit > 4 * cus and step.status == 0
+    lay = case.layout
+    ids, outs, _, rl = oracle_requests(step, "nvfp4", topk, 2.0, range(len(lay.seq_lens)))
+    m = _oracle_ids_matrix(ids, R, topk)
+    # row 3: one slot replaced by an id past its causal blocks; row 10: an id past max_blocks
+    nb3 = (int(rl[3]) + 127) // 128
+    m_bad = m.copy()
+    slot3 = int(np.argmax(m[3] < 0)) if (m[3] < 0).any() else topk - 1
+    m_bad[3, slot3] = nb3
+    m_bad[10, topk - 1] = lay.max_blocks + 5
+    # row 20's first selected block on a page outside the cache
+    b20 = int(step.rows.row_req[20].item())
+    blk = int(m[20, 0])
+    bt = step.bt.clone()
+    bt[b20, blk] = lay.num_pages + 11
+    step.bt = bt
+    got, st = _attend(gpu, step, m_bad, 2.0)
+    assert st & gpu.DEV_BITS["BAD_BLOCK_ID"] and st & gpu.DEV_BITS["BAD_PAGE"]
+    from oracle import path as Pth
+    wc_q = F.bf16_to_f64(W.bf16_bits(case.q))
+    row_req = step.rows.row_req.cpu().numpy()
+    planes = {}
+    affected = set()
+    for r, want in outs.items():
+        b = int(row_req[r])
+        nb = (int(rl[r]) + 127) // 128
+        kept = [int(j) for j in m_bad[r] if 0 <= j < nb and not (b == b20 and j == blk)]
+        if len(kept) != int((m[r] >= 0).sum()):    # a skipped block: the oracle over the rest
+            affected.add(r)
+            if b not in planes:
+                lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
+                planes[b] = (F.dequantize("nvfp4", *F.quantize("nvfp4", W.bf16_bits(case.k[lo:hi]))),
+                             F.dequantize("nvfp4", *F.quantize("nvfp4", W.bf16_bits(case.v[lo:hi]))))
+            want = Pth.attend_row(wc_q[r], planes[b][0], planes[b][1], kept, int(rl[r]), 2.0)
+        assert max_rel_err(got[r], want) <= TOL, r
+    assert {10, 20} <= affected   # row 3 put its bad id in an empty slot
+
+
+def test_attend_mxfp4_extreme_scales(gpu):
+    """MXFP4 K / V groups whose E8M0 scales lie far outside fp16's range (amax about 2^18,
+    scale byte 143; amax about 2^-28, byte 97): the attention decodes to bf16, exact for
+    every byte a store writes, and matches the oracle within 5e-3."""
+    case = W.make_case(CFG0, DEV, seq_lens=[3000, 900], q_len=2, G=16)
+    tok = torch.arange(case.k.shape[0], device=DEV)
+    big_k = ((tok // 128) % 3 == 0).to(torch.float32) * (2.0 ** 14 - 1) + 1
+    small_k = torch.where((tok // 128) % 3 == 1, 2.0 ** -30, 1.0)
+    big_v = ((tok // 64) % 4 == 1).to(torch.float32) * (2.0 ** 14 - 1) + 1
+    small_v = torch.where((tok // 64) % 4 == 2, 2.0 ** -30, 1.0)
+    case.k = (case.k.float() * (big_k * small_k)[:, None]).to(torch.bfloat16)
+    case.v = (case.v.float() * (big_v * small_v)[:, None]).to(torch.bfloat16)
+    sm = 2.0 ** -12   # keeps the logits of the 2^14-scaled keys of order one
+    step = run_gpu_step(gpu, CFG0, DEV, topk=8, fmt="mxfp4", case=case, sm_scale=sm)
+    assert step.status == 0, hex(step.status)
+    sc = step.cache.planes["k"][1].cpu().numpy()
+    assert sc.max() >= 142 and sc[sc > 0].min() <= 102      # outside fp16's exact range
+    ids, outs, _, _ = oracle_requests(step, "mxfp4", 8, sm, range(2))
+    got, st = _attend(gpu, step, _oracle_ids_matrix(ids, 4, 8), sm)
+    assert st == 0
+    worst = max(max_rel_err(got[r], want) for r, want in outs.items())
+    assert worst <= TOL, worst
+
+
+def test_attend_mxfp4_unstorable_scale_flagged(gpu):
+    """An E8M0 scale byte above 252 (no store writes one) decodes to infinity: the
+    affected outputs are written as 0 and the range bit is set; nothing is NaN."""
+    step = run_gpu_step(gpu, CFG0, DEV, seq_lens=[2000], q_len=1, G=16, topk=4, fmt="mxfp4")
+    assert step.status == 0
+    blk = int(step.ids[0, 0].item())
+    page = int(step.bt[0, blk].item())
+    step.cache.planes["k"][1][page, 3, :] = 254
+    ids = step.ids.cpu().numpy()
+    got, st = _attend(gpu, step, ids, 1.0)
+    assert st & gpu.DEV_BITS["RANGE"]
+    assert np.isfinite(got).all()
