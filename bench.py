@@ -28,8 +28,29 @@ METRIC = "decode rows/s + achieved HBM GB/s (store+score+top-k+attend), 8 req x 
 HBM_PEAK_GBS = 8000.0
 PRODUCER_ROTARY_DIM = 64   # rotary dims of the producer measurement (half the head)
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}  # dense, MI355X
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "index_topk_b8x8_150k_traffic.json")
-INDEX_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/index_topk.hip", "block_sparse_decode_nvfp4_amd/csrc/fp4.hpp"]
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/" + f for f in (
+    "index_topk.hip", "attend_body.hpp", "attend.hip", "store.hip", "rows.hip", "rows_body.hpp", "quant.hpp",
+    "fp4.hpp", "launch.hpp")]
+
+
+def traffic_file(workload):
+    return os.path.join(PROFILES, f"decode_step_{workload}_traffic.json")
+
+
+def trace_file(workload):
+    return os.path.join(PROFILES, f"decode_step_{workload}_kernels.json")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def log(*a):
@@ -105,8 +126,12 @@ def step_bytes(cfg, lay, ids_np, G):
     queries = R * 256 + R * G * 256                                # q_idx + q (bf16)
     outs = R * G * 128 * 4 + 2 * R * cfg.topk * 4                  # fp32 out + ids (write + read)
     other = store + tables + queries + outs
+    index_call = index + tables + R * 256
+    # m3s_index_topk_attend: the index call's bytes, the distinct selected K/V, the main
+    # query, the fp32 output and the ids it writes
+    fused_call = index_call + attend + R * G * 256 + R * G * 128 * 4 + R * cfg.topk * 4
     return {"index": index, "attend": attend, "store": store, "other": other,
-            "total": index + attend + other, "index_call": index + tables + R * 256}
+            "total": index + attend + other, "index_call": index_call, "fused_call": fused_call}
 
 
 def cpu_baseline(cfg, case, nreq, log_fn):
@@ -143,7 +168,7 @@ def cpu_baseline(cfg, case, nreq, log_fn):
     dt = time.perf_counter() - t0
     rows = int(sum(int(lay.cu_q[b + 1] - lay.cu_q[b]) for b in reqs))
     log_fn(f"[cpu baseline] oracle step on {nreq} request(s) ({rows} rows): {dt:.2f} s")
-    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+    return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{nreq} of {len(lay.seq_lens)} requests ({rows} rows) of the same workload, full step "
                       f"(store of their rows, row map, float64 dequantize + score of every causal block, "
                       f"sort top-k, float64 softmax attention), history quantization untimed; {dt:.1f} s"}
@@ -152,66 +177,231 @@ def cpu_baseline(cfg, case, nreq, log_fn):
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
 
 
-def _pmc_per_dispatch(path, counter):
-    """Average counter value (KiB) per dispatch, by kernel name, from a rocprofv3 counter CSV."""
+FRONT_KERNELS = ("store_rows_kernel", "store_kernel", "decode_rows_kernel", "prefill_rows_kernel")
+
+
+def kernel_short(name):
+    """'void m3s::index_scan_kernel<1, 1, 16, 1>(m3s::IndexArgs)' -> 'index_scan_kernel<1, 1, 16, 1>'."""
+    n = name.strip()
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):       # the argument list starts at the first '(' outside '<...>'
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    n = n[:cut]
+    return n[5:] if n.startswith("m3s::") else n
+
+
+def _base(short):
+    return short.split("<", 1)[0]
+
+
+def step_sequences(dispatches):
+    """dispatches: [(dispatch order, short kernel name, payload)] of the library's kernels.
+    Splits them at each front kernel (the store that opens a step) and returns the most
+    common kernel-name sequence and the list of runs that have it."""
+    dispatches = sorted(dispatches, key=lambda t: t[0])
+    runs, cur = [], None
+    for d in dispatches:
+        if _base(d[1]) in FRONT_KERNELS and (cur is None or _base(cur[-1][1]) not in FRONT_KERNELS):
+            if cur:
+                runs.append(cur)
+            cur = [d]
+        elif cur is not None:
+            cur.append(d)
+    if cur:
+        runs.append(cur)
+    count = {}
+    for r in runs:
+        key = tuple(x[1] for x in r)
+        count[key] = count.get(key, 0) + 1
+    if not count:
+        raise SystemExit("no step found in the profile")
+    best = max(count, key=lambda k: (count[k], len(k)))
+    return list(best), [r for r in runs if tuple(x[1] for x in r) == best]
+
+
+def _pmc_dispatches(path, counter):
+    """[(dispatch id, short name, counter value in KiB summed over the dispatch)] from a
+    rocprofv3 counter CSV."""
     import csv
-    acc = {}
+    acc, names = {}, {}
     with open(path, newline="") as f:
         for row in csv.DictReader(f):
             if row.get("Counter_Name") != counter:
                 continue
-            key = (row["Kernel_Name"], row.get("Dispatch_Id") or row.get("Correlation_Id"))
-            acc[key] = acc.get(key, 0.0) + float(row["Counter_Value"])
-    per = {}
-    for (name, _), v in acc.items():
-        per.setdefault(name, []).append(v)
-    return {n: (sum(v) / len(v), len(v)) for n, v in per.items()}
+            did = int(row.get("Dispatch_Id") or row.get("Correlation_Id"))
+            acc[did] = acc.get(did, 0.0) + float(row["Counter_Value"])
+            names[did] = kernel_short(row["Kernel_Name"])
+    return [(d, names[d], acc[d]) for d in acc]
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return 0.5 * (v[(n - 1) // 2] + v[n // 2]) if n else 0.0
 
 
 def ingest_pmc(fetch_csv, write_csv, config):
-    """HBM bytes per m3s_index_topk launch, from FETCH_SIZE / WRITE_SIZE counters scaled by
-    what the same counters read for the calibration copy (COPY_BYTES read + COPY_BYTES
-    written)."""
+    """HBM bytes of every kernel of the decode step, from FETCH_SIZE / WRITE_SIZE counters
+    scaled by what the same counters read for the calibration copy (COPY_BYTES read +
+    COPY_BYTES written). Per kernel: the median over the steps of the graph replays."""
     import workloads as W
     cfg = W.config(int(config) if config.isdigit() else config)
-    fetch = _pmc_per_dispatch(fetch_csv, "FETCH_SIZE")
-    write = _pmc_per_dispatch(write_csv, "WRITE_SIZE")
+    fd = _pmc_dispatches(fetch_csv, "FETCH_SIZE")
+    wd = _pmc_dispatches(write_csv, "WRITE_SIZE")
 
-    def pick(d, key):
-        hits = [(n, v) for n, v in d.items() if key in n]
-        if not hits:
-            raise SystemExit(f"no kernel matching {key!r} in the counter file")
-        return max(hits, key=lambda t: t[1][1])[1]
+    def copy_kib(ds):
+        v = [x[2] for x in ds if "neg" in x[1]]
+        if not v:
+            raise SystemExit("no calibration copy (torch.neg) in the counter file")
+        return _median(v)
 
-    copy_f, _ = pick(fetch, "neg")
-    copy_w, _ = pick(write, "neg")
+    copy_f, copy_w = copy_kib(fd), copy_kib(wd)
     f_scale = COPY_BYTES / (copy_f * 1024.0)
     w_scale = COPY_BYTES / (copy_w * 1024.0)
-    parts = {}
-    for k in ("index_scan_kernel", "index_select_kernel"):
-        fk, nf = pick(fetch, k)
-        wk, nw = pick(write, k)
-        parts[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "dispatches": [nf, nw],
-                    "fetch_bytes": round(fk * 1024.0 * f_scale), "write_bytes": round(wk * 1024.0 * w_scale)}
-    total = sum(v["fetch_bytes"] + v["write_bytes"] for v in parts.values())
-    rec = {"workload": cfg.name, "source_sha": source_sha(INDEX_SOURCES), "bytes_per_launch": total,
-           "kernels": parts,
+    lib = lambda ds: [x for x in ds if "neg" not in x[1] and "::" not in x[1]]
+    seq_f, runs_f = step_sequences(lib(fd))
+    seq_w, runs_w = step_sequences(lib(wd))
+    if seq_f != seq_w:
+        raise SystemExit(f"the two passes ran different steps: {seq_f} / {seq_w}")
+    parts = []
+    for i, name in enumerate(seq_f):
+        fk = _median([r[i][2] for r in runs_f])
+        wk = _median([r[i][2] for r in runs_w])
+        parts.append({"kernel": name, "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                      "steps": [len(runs_f), len(runs_w)],
+                      "fetch_bytes": round(fk * 1024.0 * f_scale), "write_bytes": round(wk * 1024.0 * w_scale)})
+    call = [p for p in parts if _base(p["kernel"]) not in FRONT_KERNELS]
+    rec = {"workload": cfg.name, "source_sha": source_sha(KERNEL_SOURCES),
+           "step_kernels": parts,
+           "fused_call_bytes": sum(p["fetch_bytes"] + p["write_bytes"] for p in call),
+           "step_bytes": sum(p["fetch_bytes"] + p["write_bytes"] for p in parts),
            "calibration": {"copy_bytes_each_way": COPY_BYTES, "copy_fetch_kib": round(copy_f, 1),
                            "copy_write_kib": round(copy_w, 1), "fetch_scale": round(f_scale, 4),
                            "write_scale": round(w_scale, 4)},
            "commands": ["cd /tmp && export TMPDIR=/tmp  # $R = repository root",
                         *[f"timeout -s KILL 150 rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/pmc_{d} "
-                          f"-o run -- python -u $R/bench.py --config {cfg.name} --steps 5 --warmup 2 "
+                          f"-o run -- python -u $R/bench.py --config {cfg.name} --steps 20 --warmup 2 "
                           f"--stage-reps 10 --no-cpu --copy-calibration" for c, d in (("FETCH_SIZE", "fetch"),
                                                                                      ("WRITE_SIZE", "write"))],
                         f"python bench.py --config {cfg.name} --ingest-pmc "
                         f"gpurun_out/pmc_fetch/run_counter_collection.csv "
                         f"gpurun_out/pmc_write/run_counter_collection.csv"]}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    path = traffic_file(cfg.name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     log(json.dumps(rec, indent=1))
+
+
+def ingest_trace(trace_csv, config):
+    """Per-kernel durations of the decode step from a rocprofv3 kernel trace: the median,
+    over the steps of the graph replays, of each kernel's duration, the step's span (first
+    start to last end) and the gap before the next step."""
+    import csv
+    import workloads as W
+    cfg = W.config(int(config) if config.isdigit() else config)
+    ds = []
+    with open(trace_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            name = kernel_short(row["Kernel_Name"])
+            if "::" in name or not name:
+                continue
+            ds.append((int(row["Dispatch_Id"]), name, (int(row["Start_Timestamp"]), int(row["End_Timestamp"]),
+                                                        int(row["Grid_Size_X"]) // max(1, int(row["Workgroup_Size_X"])))))
+    seq, runs = step_sequences(ds)
+    runs.sort(key=lambda r: r[0][2][0])
+    kern = []
+    for i, name in enumerate(seq):
+        dur = [(r[i][2][1] - r[i][2][0]) / 1e3 for r in runs]
+        kern.append({"kernel": name, "workgroups": runs[0][i][2][2], "median_us": round(_median(dur), 2),
+                     "mean_us": round(sum(dur) / len(dur), 2)})
+    span = [(r[-1][2][1] - r[0][2][0]) / 1e3 for r in runs]
+    starts = [r[0][2][0] for r in runs]
+    ends = [r[-1][2][1] for r in runs]
+    gaps = [(starts[i + 1] - ends[i]) / 1e3 for i in range(len(runs) - 1) if starts[i + 1] > ends[i]]
+    rec = {"workload": cfg.name, "source_sha": source_sha(KERNEL_SOURCES), "steps": len(runs),
+           "step_kernels": kern, "step_span_median_us": round(_median(span), 2),
+           "gap_to_next_step_median_us": round(_median(gaps), 2) if gaps else None,
+           "commands": ["cd /tmp && export TMPDIR=/tmp  # $R = repository root",
+                        f"timeout -s KILL 200 rocprofv3 --kernel-trace --stats --output-format csv -d "
+                        f"$R/gpurun_out/prof_{cfg.name} -o run -- python3 -u $R/bench.py --config {cfg.name} "
+                        f"--steps 100 --warmup 10 --no-cpu",
+                        f"python bench.py --config {cfg.name} --ingest-trace "
+                        f"gpurun_out/prof_{cfg.name}/run_kernel_trace.csv"]}
+    path = trace_file(cfg.name)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    log(json.dumps(rec, indent=1))
+
+
+def load_record(path, workload):
+    """A committed profile record, if it was taken on the current kernel code."""
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES) or rec.get("workload") != workload:
+        return None
+    return rec
+
+
+def ceilings(m3s, cfg, dev, layers):
+    """Page-read ceilings of the index scan's access pattern (m3s_probe_page_reads): the
+    workload's index planes (one per layer, as in the bench), every causal page read once
+    per launch in a random order, then the same pages in address order; launches cycle
+    over the layers so that no launch is served from the Infinity Cache."""
+    import numpy as np
+    import torch
+    import workloads as W
+    lay = W.make_layout(cfg.seq_lens, cfg.q_len, cfg.seed)
+    P = lay.num_pages
+    npages = int(lay.nblk.sum())
+    rng = np.random.default_rng(1234)
+    planes = [(torch.randint(0, 255, (P, 128, 64), dtype=torch.uint8, device=dev),
+               torch.randint(0, 255, (P, 128, 8), dtype=torch.uint8, device=dev)) for _ in range(layers)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.zeros(cus, dtype=torch.int32, device=dev)
+    orders = {"random": torch.as_tensor(rng.permutation(P)[:npages].astype(np.int32), device=dev),
+              "sequential": torch.arange(npages, dtype=torch.int32, device=dev)}
+    res = {"workload": cfg.name, "pages_per_launch": npages, "bytes_per_launch": npages * 128 * 72,
+           "layers_cycled": layers, "cus": cus}
+    reps = 40
+    for order, pages in orders.items():
+        for mode in (0, 1):
+            for L in range(layers):   # warm-up; the page ids are checked once, here
+                m3s.m3s_probe_page_reads(planes[L][0], planes[L][1], pages, mode, sink, check=True)
+            best = None
+            for trial in range(3):
+                ea = torch.cuda.Event(enable_timing=True)
+                eb = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(3_000_000)
+                ea.record()
+                for i in range(reps):
+                    L = i % layers
+                    m3s.m3s_probe_page_reads(planes[L][0], planes[L][1], pages, mode, sink, check=False)
+                eb.record()
+                torch.cuda.synchronize()
+                t = ea.elapsed_time(eb) / reps
+                best = t if best is None else min(best, t)
+            key = f"{order}_scales_{'2B' if mode == 0 else '16B'}"
+            res[key] = {"us_per_launch": round(best * 1e3, 2),
+                        "gbs": round(npages * 128 * 72 / (best * 1e-3) / 1e9, 1)}
+            log(f"[ceilings] {key}: {best * 1e3:.2f} us, {res[key]['gbs']:.0f} GB/s")
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -233,9 +423,19 @@ def main():
     ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE run, "
                          "WRITE_SIZE run) of 'bench.py --copy-calibration' into the traffic record")
+    ap.add_argument("--ingest-trace", metavar="TRACE_CSV",
+                    help="no GPU: turn a rocprofv3 kernel_trace.csv of the bench into the per-kernel record")
+    ap.add_argument("--graph-layers", type=int, default=0,
+                    help="steps captured in one HIP graph (default: all --layers, one step per layer cache, "
+                         "as a model's decode graph holds its layers; 1: one graph per step)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="measure the page-read ceilings of the index scan's access pattern and exit")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.config)
+        return
+    if args.ingest_trace:
+        ingest_trace(args.ingest_trace, args.config)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -253,6 +453,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = W.config(int(args.config) if args.config.isdigit() else args.config)
+    if args.ceilings:
+        ceilings(m3s, cfg, dev, max(1, args.layers))
+        return
     log(f"[bench] workload {cfg.name}: {cfg.description}")
     t_setup = time.perf_counter()
     case = W.make_case(cfg, dev)
@@ -329,7 +532,9 @@ def main():
         log(f"[bench] device status {st:#x}")
         sys.exit(3)
 
-    # ---- graphs: one per layer (the whole step)
+    # ---- graphs: one per layer (the whole step), and one holding GL consecutive steps over
+    # the layer caches in turn, as a model's decode graph holds its layers (the launch of a
+    # graph then comes once per GL steps instead of once per step)
     side = torch.cuda.Stream()
     graphs = []
     for c in caches:
@@ -337,9 +542,26 @@ def main():
         with torch.cuda.graph(g, stream=side):
             run_step(c)
         graphs.append(g)
+    GL = NL if args.graph_layers <= 0 else min(args.graph_layers, NL)
+    multi = None
+    if GL > 1:
+        multi = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(multi, stream=side):
+            for c in caches[:GL]:
+                run_step(c)
     torch.cuda.synchronize()
     log(f"[bench] setup {time.perf_counter() - t_setup:.1f} s; {NL} layers x {lay.num_pages} pages; "
-        f"rows {R}, G {G}, top-k {cfg.topk}")
+        f"rows {R}, G {G}, top-k {cfg.topk}; {GL} steps per graph")
+
+    def run_steps(k):
+        """k steps: k // GL replays of the multi-step graph, then single-step graphs."""
+        done = 0
+        if multi is not None:
+            for _ in range(k // GL):
+                multi.replay()
+            done = (k // GL) * GL
+        for i in range(done, k):
+            graphs[i % NL].replay()
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -350,22 +572,32 @@ def main():
         del src, dst
         log(f"[bench] calibration copy: {COPY_BYTES >> 20} MiB read + written, 3 launches")
 
-    # ---- timed region: K steps, graph replays cycling over the layers
-    for i in range(args.warmup):
-        graphs[i % NL].replay()
+    # ---- timed region: exactly K steps
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for i in range(args.steps):
-        graphs[i % NL].replay()
+    run_steps(args.steps)
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / args.steps
     st = int(status.item())
+
+    # one graph per step, for comparison: the same steps with a graph launch each
+    n1 = min(max(args.steps, 1), 8 * NL)
+    e2 = torch.cuda.Event(enable_timing=True)
+    e3 = torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(5_000_000)
+    e2.record()
+    for i in range(n1):
+        graphs[i % NL].replay()
+    e3.record()
+    torch.cuda.synchronize()
+    ms_single = e2.elapsed_time(e3) / n1
 
     # ---- per-replay distribution: an event between consecutive replays, the whole run
     # queued behind a GPU spin so that the host's enqueue rate does not show; the events'
@@ -446,30 +678,36 @@ def main():
     by = step_bytes(cfg, lay, ids_np, G)
     rows_per_s = R / (ms_per_step / 1e3)
     gbs_step = by["total"] / (ms_per_step / 1e3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (event), wall {wall / args.steps * 1e6:.2f} us/step")
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step (event), wall {wall / args.steps * 1e6:.2f} us/step; "
+        f"{ms_single * 1e3:.2f} us/step with one graph launch per step")
     log(f"[bench] per replay ({nd} replays, events between them): p10 {step_dist['p10']:.2f}, "
         f"median {step_dist['median']:.2f}, p90 {step_dist['p90']:.2f} us")
     log(f"[bench] algorithmic bytes/step: index {by['index'] / 1e6:.2f} MB, attend {by['attend'] / 1e6:.2f} MB, "
         f"other {by['other'] / 1e6:.2f} MB, total {by['total'] / 1e6:.2f} MB -> {gbs_step:.0f} GB/s")
-    roofline = None
+    roofline = roofline_index = kernel_split = None
+    trace = load_record(trace_file(cfg.name), cfg.name)
+    traffic = load_record(traffic_file(cfg.name), cfg.name)
     if stage_ms:
         names = [nm for nm, _ in stages]
         log("[bench] stages (us, each stage launched back to back): " +
             ", ".join(f"{nm} {v * 1e3:.2f}" for nm, v in zip(names, stage_ms)))
         t_idx = stage_ms[1] / 1e3
-        ach = by["index_call"] / t_idx / 1e9
-        traffic = None
-        if os.path.exists(TRAFFIC_FILE):
-            try:
-                tf = json.load(open(TRAFFIC_FILE))
-                if tf.get("source_sha") == source_sha(INDEX_SOURCES) and tf.get("workload") == cfg.name:
-                    traffic = tf.get("bytes_per_launch")
-            except Exception:
-                traffic = None
+        t_fused = stage_ms[3] / 1e3
+        call_kernels = None
+        if trace:
+            call_kernels = [k["kernel"] for k in trace["step_kernels"] if _base(k["kernel"]) not in FRONT_KERNELS]
+        # the call the step runs: m3s_index_topk_attend, its algorithmic bytes over its
+        # launch time (HIP events on its stream)
+        ach = by["fused_call"] / t_fused / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": "m3s_index_topk (index_scan + index_select kernels)",
-                    "launch_us": round(stage_ms[1] * 1e3, 2), "bytes_per_launch": by["index_call"]}
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": traffic["fused_call_bytes"] if traffic else None,
+                    "kernel": "m3s_index_topk_attend" + (f" ({', '.join(call_kernels)})" if call_kernels else ""),
+                    "launch_us": round(stage_ms[3] * 1e3, 2), "bytes_per_launch": by["fused_call"]}
+        ach_i = by["index_call"] / t_idx / 1e9
+        roofline_index = {"kernel": "m3s_index_topk (scan + select)", "achieved": round(ach_i, 1),
+                          "frac": round(ach_i / HBM_PEAK_GBS, 4), "launch_us": round(stage_ms[1] * 1e3, 2),
+                          "bytes_per_launch": by["index_call"]}
         if prefill:
             # A prefill chunk's pages stay in the caches while every 16-row group re-scores
             # them: the scan is bound by the matrix cores, not HBM. Algorithmic work is one
@@ -482,6 +720,19 @@ def main():
                         "frac": round(tf_s / peak, 4), "traffic": None,
                         "kernel": "m3s_index_topk (index_scan + index_select kernels)",
                         "launch_us": round(stage_ms[1] * 1e3, 2), "flop_per_launch": flop}
+    if trace:
+        # per-kernel durations of the step from the committed kernel trace (taken on the
+        # current kernel code), with the algorithmic bytes of the kernels that have them
+        kb = {"index_scan_kernel": by["index_call"]}
+        kernel_split = []
+        for k in trace["step_kernels"]:
+            b = kb.get(_base(k["kernel"]))
+            e = {"kernel": k["kernel"], "us": k["median_us"]}
+            if b:
+                e["bytes"] = b
+                e["frac"] = round(b / (k["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            kernel_split.append(e)
+        log("[bench] kernel split (profiles/): " + ", ".join(f"{e['kernel']} {e['us']}" for e in kernel_split))
 
     cpu = None
     if not args.no_cpu and not prefill:  # the oracle on a 4096-row chunk takes hours
@@ -508,11 +759,15 @@ def main():
                    "front": "m3s_store_and_rows" if fused_front else "separate store and row-map calls",
                    "topk_attend": "m3s_index_topk_attend" if fused_attend else "separate m3s_index_topk, m3s_sparse_attend"},
         "hbm_gbs_step": round(gbs_step, 1),
+        "steps_per_graph": GL,
+        "us_per_step_one_graph_each": round(ms_single * 1e3, 2),
         "step_us_dist": step_dist,
         "bytes_per_step": by["total"],
         "stage_us": None if not stage_ms else {nm: round(v * 1e3, 2) for (nm, _), v in zip(stages, stage_ms)},
         "device_status": st,
         "roofline": roofline,
+        "roofline_index_topk": roofline_index,
+        "kernel_split": kernel_split,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -30,11 +30,13 @@ TOPK_TIE_HIGH_ID = 1
 DEV_BITS = {
     "BAD_SLOT": 1 << 0, "BAD_ROWS": 1 << 1, "BAD_LENGTH": 1 << 2, "BAD_PAGE": 1 << 3,
     "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6, "BAD_POSITION": 1 << 7,
+    "RANGE": 1 << 8,
 }
 
 EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_qknorm_rope_store",
            "m3s_index_topk", "m3s_sparse_attend", "m3s_index_topk_attend",
-           "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version")
+           "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version",
+           "m3s_probe_page_reads")
 MAX_GROUPS = 4096
 GROUP_ROWS = 64
 
@@ -91,6 +93,7 @@ def load(path: str | None = None):
         "m3s_read_device_status": (I32, [V, V, V]),
         "m3s_status_string": (ctypes.c_char_p, [I32]),
         "m3s_version": (I32, []),
+        "m3s_probe_page_reads": (I32, [V, V, V, I32, I32, V, I32, V]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -416,6 +419,27 @@ def m3s_index_topk_attend(cache: Cache, q_idx, q, block_table, max_blocks: int, 
                                       _ptr(workspace), workspace.numel(), _ptr(dev_status), _stream(stream))
     _check("m3s_index_topk_attend", st)
     return topk_ids, out
+
+
+def m3s_probe_page_reads(payload, scales, pages, mode: int, sink, stream=None, check: bool = True):
+    """Measurement only: read the listed pages with the index scan's load pattern
+    (see include/m3s.h). Every page id must lie inside the planes: with check=True the
+    ids are checked here (a device-to-host read); a timing loop checks once, then passes
+    check=False."""
+    torch = _torch()
+    _need(payload, "payload", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    _need(pages, "pages", torch.int32)
+    _need(sink, "sink", torch.int32)
+    P = payload.shape[0]
+    if payload.numel() != P * PAGE * 64 or scales.numel() != P * PAGE * 8:
+        raise ValueError("payload must be [P, 128, 64] and scales [P, 128, 8]")
+    # host-side bounds check of every page id (the kernel trusts them)
+    if check and pages.numel() and (int(pages.min()) < 0 or int(pages.max()) >= P):
+        raise ValueError("page id outside the planes")
+    st = load().m3s_probe_page_reads(_ptr(payload), _ptr(scales), _ptr(pages), pages.numel(), mode, _ptr(sink),
+                                     sink.numel(), _stream(stream))
+    _check("m3s_probe_page_reads", st)
 
 
 def m3s_read_device_status(dev_status, stream=None) -> int:

@@ -100,8 +100,12 @@ enum {
   M3S_DEV_BAND_OVERFLOW = 1u << 6, /* index_topk: more than 1024 blocks inside a row's
                                       uncertainty band; that row fell back to the
                                       approximate scores */
-  M3S_DEV_BAD_POSITION = 1u << 7   /* qknorm_rope_store: position outside [0, max_pos);
+  M3S_DEV_BAD_POSITION = 1u << 7,  /* qknorm_rope_store: position outside [0, max_pos);
                                       that token's outputs are left unwritten */
+  M3S_DEV_RANGE = 1u << 8          /* attend: an output element was not finite in fp32 (logits
+                                      or sums beyond the fp32 range; MXFP4 scale bytes 253
+                                      and 254, which no store writes, decode to infinity);
+                                      that element is written as 0 */
 };
 
 /* Flags of m3s_index_topk. */
@@ -112,8 +116,9 @@ enum {
 
 /*
  * One KV head's paged cache (host struct; the plane pointers are device
- * pointers). Reading of [ATOM-2746] Summary ("k/v and k_scale/v_scale are
- * uint8 planes") and [VLLM-64198] Claims (page = [128 x 64 B][128 x 4 B]):
+ * pointers). Reading of [ATOM-2746] Summary (K, V and their scales are
+ * separate uint8 planes) and [VLLM-64198] Claims (an MXFP4 page holds 128
+ * rows of 64 B of codes, then 128 rows of 4 B of scales):
  * each tensor (K, V, index K) has a payload plane and a scale plane, page
  * major; slot s = page * 128 + offset lives at
  *     payload[page][offset][0..64)   byte j = code(2j) | code(2j+1) << 4
@@ -324,9 +329,11 @@ m3s_status m3s_index_topk(const m3s_cache* cache, const uint16_t* q_idx, int64_t
  *   workspace    device scratch of m3s_workspace_bytes(M3S_OP_SPARSE_ATTEND, ...)
  *                (split partials; none needed when topk <= 4). Calls that share
  *                a workspace must not overlap in time.
- * Computation: K and V are decoded exactly to fp16 (code * scale), the query is
- * scaled by a power of two into fp16 range, QK^T and PV run on fp16 MFMA with
- * fp32 accumulation, softmax in fp32. Each workgroup takes 4 of a row's blocks
+ * Computation: K and V are decoded exactly (code * scale): NVFP4 to fp16, with
+ * the query scaled by a power of two into fp16 range, QK^T and PV on fp16 MFMA;
+ * MXFP4 to bf16 (the only 16-bit type whose range holds every E8M0 scale a
+ * store writes), the bf16 query as is, QK^T on bf16 MFMA and PV with P split
+ * into two bf16 terms (16 significant bits); fp32 accumulation and softmax. Each workgroup takes 4 of a row's blocks
  * (a split); a combine pass merges the splits' partials (split-K online
  * softmax).
  */
@@ -375,6 +382,21 @@ const char* m3s_status_string(m3s_status status);
 
 /* M3S_VERSION of the built library. */
 int32_t m3s_version(void);
+
+/*
+ * m3s_probe_page_reads - measurement only, not part of the decode path: reads
+ * num_units whole NVFP4 pages (payload [P][128][64] and scales [P][128][8], page
+ * pages[u] for unit u) with the index scan's load pattern and nothing else, so its
+ * time gives the memory system's ceiling for that pattern. One 16-wave workgroup per
+ * sink entry (pass the CU count); each writes one folded word to sink[num_sink].
+ * mode 0: 2-byte scale loads per 16-token tile, as the NVFP4 scan loads them;
+ * mode 1: one 16-byte load per lane over the page's 1 KB scale block.
+ * Returns M3S_ERR_INVALID_ARG for null pointers, num_units < 0, num_sink < 1 or
+ * another mode. Page ids are not checked: every pages[u] must lie in the planes.
+ */
+m3s_status m3s_probe_page_reads(const uint8_t* payload, const uint8_t* scales, const int32_t* pages,
+                                int32_t num_units, int32_t mode, uint32_t* sink, int32_t num_sink,
+                                hipStream_t stream);
 
 #ifdef __cplusplus
 }

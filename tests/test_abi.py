@@ -255,3 +255,15 @@ def test_index_topk_attend_validation(lib):
         a256(m3s.m3s_workspace_bytes(m3s.OP_SPARSE_ATTEND, 2, 1, 64, 16, 16)) + 256
     assert f(wsb=need - 1) == Wk
     assert f(r=_rows(nreq=0, nrows=0)) == m3s.OK        # no rows: nothing to do
+
+
+def test_probe_rejects_bad_arguments(lib):
+    """The measurement-only page-read probe validates on the host and launches nothing."""
+    import ctypes
+    f = lib.m3s_probe_page_reads
+    one = ctypes.c_void_p(16)
+    assert f(None, one, one, 1, 0, one, 1, None) == m3s.ERR_INVALID_ARG
+    assert f(one, one, one, -1, 0, one, 1, None) == m3s.ERR_INVALID_ARG
+    assert f(one, one, one, 1, 2, one, 1, None) == m3s.ERR_INVALID_ARG
+    assert f(one, one, one, 1, 0, one, 0, None) == m3s.ERR_INVALID_ARG
+    assert f(one, one, one, 0, 0, one, 1, None) == m3s.OK
