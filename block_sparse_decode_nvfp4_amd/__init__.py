@@ -36,7 +36,8 @@ DEV_BITS = {
 EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_qknorm_rope_store",
            "m3s_index_topk", "m3s_sparse_attend", "m3s_index_topk_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version",
-           "m3s_probe_page_reads")
+           "m3s_probe_page_reads", "m3s_index_topk_attend_noalloc")
+NOALLOC_SCRATCH_BYTES = 32 << 20
 MAX_GROUPS = 4096
 GROUP_ROWS = 64
 
@@ -94,6 +95,8 @@ def load(path: str | None = None):
         "m3s_status_string": (ctypes.c_char_p, [I32]),
         "m3s_version": (I32, []),
         "m3s_probe_page_reads": (I32, [V, V, V, I32, I32, V, I32, V]),
+        "m3s_index_topk_attend_noalloc": (I32, [V, V, I64, V, I64, I64, I32, V, I32, I32, V, I32, I32, I32, I32,
+                                                F32, V, V, V, V]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -440,6 +443,36 @@ def m3s_probe_page_reads(payload, scales, pages, mode: int, sink, stream=None, c
     st = load().m3s_probe_page_reads(_ptr(payload), _ptr(scales), _ptr(pages), pages.numel(), mode, _ptr(sink),
                                      sink.numel(), _stream(stream))
     _check("m3s_probe_page_reads", st)
+
+
+def m3s_index_topk_attend_noalloc(cache: Cache, q_idx, q, block_table, max_blocks: int, rows: Rows, topk: int,
+                                  sm_scale: float, flags: int = 0, topk_ids=None, out=None, dev_status=None,
+                                  stream=None, init_blocks: int = 0, local_blocks: int = 0):
+    """m3s_index_topk_attend with the library's own scratch buffer as the workspace (no
+    device allocation inside the call; outputs are still the caller's). Returns
+    (topk_ids, out)."""
+    torch = _torch()
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(q, "q", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    if q_idx.dim() != 2 or q_idx.stride(1) != 1 or q_idx.shape[1] < HEAD_DIM:
+        raise ValueError("q_idx must be [R, >=128] with unit inner stride")
+    if q.dim() != 3 or q.stride(2) != 1 or q.shape[2] < HEAD_DIM:
+        raise ValueError("q must be [R, G, >=128] with unit inner stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, stride] with unit inner stride")
+    G = q.shape[1]
+    dev = q.device
+    if topk_ids is None:
+        topk_ids = torch.empty((rows.num_rows, topk), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((rows.num_rows, G, HEAD_DIM), dtype=torch.float32, device=dev)
+    st = load().m3s_index_topk_attend_noalloc(cache.ref(), _ptr(q_idx), q_idx.stride(0), _ptr(q), q.stride(0),
+                                              q.stride(1), G, _ptr(block_table), block_table.stride(0), max_blocks,
+                                              rows.ref(), topk, flags, init_blocks, local_blocks, float(sm_scale),
+                                              _ptr(topk_ids), _ptr(out), _ptr(dev_status), _stream(stream))
+    _check("m3s_index_topk_attend_noalloc", st)
+    return topk_ids, out
 
 
 def m3s_read_device_status(dev_status, stream=None) -> int:

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libm3s.so")
 
-HIP_SOURCES = ["store.hip", "producer.hip", "rows.hip", "index_topk.hip", "attend.hip", "probe.hip"]
+HIP_SOURCES = ["store.hip", "producer.hip", "rows.hip", "index_topk.hip", "attend.hip", "probe.hip", "scratch.hip"]
 HOST_SOURCES = ["api.cpp"]
 HEADERS = ["fp4.hpp", "launch.hpp", "quant.hpp", "rows_body.hpp"]
 

@@ -11,6 +11,8 @@
 #include "m3s.h"
 #include "launch.hpp"
 
+static_assert(M3S_NOALLOC_SCRATCH_BYTES == m3s::kNoallocScratchBytes, "scratch size mismatch");
+
 using namespace m3s;
 
 namespace {
@@ -79,7 +81,9 @@ const char* m3s_status_string(m3s_status s) {
     case M3S_OK: return "ok";
     case M3S_ERR_INVALID_ARG: return "invalid argument (null pointer, negative count, bad stride or alignment)";
     case M3S_ERR_UNSUPPORTED: return "unsupported shape (page/head_dim != 128, G, top-k, or size limits)";
-    case M3S_ERR_WORKSPACE: return "workspace null or smaller than m3s_workspace_bytes";
+    case M3S_ERR_WORKSPACE:
+      return "workspace null or smaller than m3s_workspace_bytes (for the no-allocation call: "
+             "more than the library's scratch)";
     case M3S_ERR_HIP: return "HIP launch failed";
     default: return "unknown status";
   }
@@ -422,12 +426,17 @@ m3s_status m3s_sparse_attend(const m3s_cache* cache, const uint16_t* q, int64_t 
   return from_hip(launch_sparse_attend(a, stream));
 }
 
-m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
-                                 const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride, int32_t num_heads,
-                                 const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
-                                 const m3s_rows* rows, int32_t topk, int32_t flags, int32_t init_blocks,
-                                 int32_t local_blocks, float sm_scale, int32_t* topk_ids, float* out,
-                                 void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// m3s_index_topk_attend on a given workspace (the caller's, or the library's scratch).
+m3s_status index_topk_attend_impl(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                                  const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride, int32_t num_heads,
+                                  const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                                  const m3s_rows* rows, int32_t topk, int32_t flags, int32_t init_blocks,
+                                  int32_t local_blocks, float sm_scale, int32_t* topk_ids, float* out,
+                                  void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
   if (!rows) return M3S_ERR_INVALID_ARG;
   if (max_blocks < 0 || rows->num_rows < 0) return M3S_ERR_INVALID_ARG;
   const size_t ni = align256(index_ws_bytes(rows->num_rows, max_blocks));
@@ -450,6 +459,39 @@ m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, 
   ia.sel_pages = reinterpret_cast<int32_t*>(ws + np);
   aa.sel_pages = ia.sel_pages;
   return from_hip(launch_index_topk_attend(ia, aa, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                                 const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride, int32_t num_heads,
+                                 const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                                 const m3s_rows* rows, int32_t topk, int32_t flags, int32_t init_blocks,
+                                 int32_t local_blocks, float sm_scale, int32_t* topk_ids, float* out,
+                                 void* workspace, size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream) {
+  return index_topk_attend_impl(cache, q_idx, q_idx_stride, q, q_row_stride, q_head_stride, num_heads, block_table,
+                                bt_stride, max_blocks, rows, topk, flags, init_blocks, local_blocks, sm_scale,
+                                topk_ids, out, workspace, workspace_bytes, dev_status, stream);
+}
+
+m3s_status m3s_index_topk_attend_noalloc(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                                         const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                                         int32_t num_heads, const int32_t* block_table, int32_t bt_stride,
+                                         int32_t max_blocks, const m3s_rows* rows, int32_t topk, int32_t flags,
+                                         int32_t init_blocks, int32_t local_blocks, float sm_scale, int32_t* topk_ids,
+                                         float* out, uint32_t* dev_status, hipStream_t stream) {
+  if (!rows || max_blocks < 0 || rows->num_rows < 0) return M3S_ERR_INVALID_ARG;
+  // sizes past the scratch are refused before anything touches the GPU
+  const size_t need = m3s_workspace_bytes(M3S_OP_INDEX_TOPK_ATTEND, rows->num_rows, rows->num_groups, max_blocks,
+                                          topk, num_heads);
+  if (need > M3S_NOALLOC_SCRATCH_BYTES) return M3S_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return M3S_ERR_HIP;
+  return index_topk_attend_impl(cache, q_idx, q_idx_stride, q, q_row_stride, q_head_stride, num_heads, block_table,
+                                bt_stride, max_blocks, rows, topk, flags, init_blocks, local_blocks, sm_scale,
+                                topk_ids, out, ws, M3S_NOALLOC_SCRATCH_BYTES, dev_status, stream);
 }
 
 m3s_status m3s_read_device_status(const uint32_t* dev_status, uint32_t* out, hipStream_t stream) {

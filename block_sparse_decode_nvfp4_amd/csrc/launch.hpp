@@ -158,6 +158,11 @@ hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream);
 hipError_t launch_attend_combine(const AttendArgs& a, hipStream_t stream);
 
+// The no-allocation entry point's scratch: a static device array of this size per GPU
+// (scratch.hip); noalloc_scratch gives its device address on the current device.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Workspace layout helpers shared by sizing and launching.
 size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks);
 size_t attend_ws_bytes(int32_t num_rows, int32_t nsplit);

@@ -369,6 +369,33 @@ m3s_status m3s_index_topk_attend(const m3s_cache* cache, const uint16_t* q_idx, 
                                  int32_t* topk_ids, float* out, void* workspace, size_t workspace_bytes,
                                  uint32_t* dev_status, hipStream_t stream);
 
+/*
+ * m3s_index_topk_attend_noalloc - for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): m3s_index_topk_attend with the workspace taken from a scratch buffer
+ * the library owns instead of an argument. The scratch is one static device array
+ * of M3S_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends; the call
+ * allocates and frees nothing. Arguments, outputs and status bits are those of
+ * m3s_index_topk_attend.
+ *   - A call whose m3s_workspace_bytes(M3S_OP_INDEX_TOPK_ATTEND, ...) exceeds
+ *     M3S_NOALLOC_SCRATCH_BYTES returns M3S_ERR_WORKSPACE and launches nothing
+ *     (32 MiB: the 8 x 8-row 150K and skewed 450K batches need about 3-4 MiB,
+ *     the 48 x 8-row lognormal batch about 23 MiB).
+ *   - Every call on one GPU uses that GPU's one scratch buffer: calls that overlap
+ *     in time on one GPU (two streams, two threads) race on it and must not be
+ *     issued; calls in one stream order are fine. The buffer keeps the last call's
+ *     contents; the kernels write every byte they read.
+ *   - The first call on a device looks the buffer's device address up
+ *     (hipGetSymbolAddress); make that first call outside graph capture.
+ */
+#define M3S_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+m3s_status m3s_index_topk_attend_noalloc(const m3s_cache* cache, const uint16_t* q_idx, int64_t q_idx_stride,
+                                         const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride,
+                                         int32_t num_heads, const int32_t* block_table, int32_t bt_stride,
+                                         int32_t max_blocks, const m3s_rows* rows, int32_t topk, int32_t flags,
+                                         int32_t init_blocks, int32_t local_blocks, float sm_scale, int32_t* topk_ids,
+                                         float* out, uint32_t* dev_status, hipStream_t stream);
+
 /* Workspace sizing (host only, pure). */
 enum { M3S_OP_INDEX_TOPK = 1, M3S_OP_SPARSE_ATTEND = 2, M3S_OP_INDEX_TOPK_ATTEND = 3 };
 size_t m3s_workspace_bytes(int32_t op, int32_t num_rows, int32_t num_reqs, int32_t max_blocks,

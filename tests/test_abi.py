@@ -267,3 +267,23 @@ def test_probe_rejects_bad_arguments(lib):
     assert f(one, one, one, 1, 2, one, 1, None) == m3s.ERR_INVALID_ARG
     assert f(one, one, one, 1, 0, one, 0, None) == m3s.ERR_INVALID_ARG
     assert f(one, one, one, 0, 0, one, 1, None) == m3s.OK
+
+
+def test_index_topk_attend_noalloc_refuses_sizes_past_the_scratch(lib):
+    """The no-allocation call refuses, on the host and before touching a device, any shape
+    whose workspace would exceed the library's scratch; bad rows are refused as in the
+    workspace call."""
+    Wk = m3s.ERR_WORKSPACE
+
+    def f(r, mb=64, k=16, G=16):
+        c = _cache(pages=1 << 20)
+        return lib.m3s_index_topk_attend_noalloc(ctypes.byref(c), FAKE, 128, FAKE, 2048, 128, G, FAKE, 8192, mb,
+                                                 None if r is None else ctypes.byref(r), k, 0, 0, 0, 1.0, FAKE,
+                                                 FAKE, None, None)
+
+    assert m3s.NOALLOC_SCRATCH_BYTES == 32 << 20
+    big = _rows(nreq=4, nrows=4096)
+    assert m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK_ATTEND, 4096, 4, 8192, 16, 16) > m3s.NOALLOC_SCRATCH_BYTES
+    assert f(big, mb=8192) == Wk
+    assert f(None) == m3s.ERR_INVALID_ARG
+    assert f(_rows(nreq=1, nrows=-1)) == m3s.ERR_INVALID_ARG
