@@ -2,9 +2,10 @@
 attend) on one MI355X, on seeded synthetic inputs shaped like the pages' workloads.
 
 One step = one sparse layer's full path for one batch: the store of the step's new
-K/V/index rows, the row map, the index top-k and the sparse attention, issued as
-m3s_store_and_rows + m3s_index_topk_attend (or, with --separate, as the four calls
-m3s_store, m3s_decode_rows, m3s_index_topk, m3s_sparse_attend). Steps are HIP-graph
+K/V/index rows, the row map, the index top-k and the sparse attention, issued as one
+m3s_decode_step call (or, with --calls two, as m3s_store_and_rows +
+m3s_index_topk_attend; with --calls separate, as the four calls m3s_store,
+m3s_decode_rows, m3s_index_topk, m3s_sparse_attend). Steps are HIP-graph
 replays; consecutive steps use different layer copies of the cache (8 by default, >= 2 GB
 in total at the default workload) so a step cannot be served from the 256 MB Infinity
 Cache left warm by the previous one - as in a real model, where each of the 60 sparse
@@ -31,7 +32,7 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}  # dense, MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/" + f for f in (
     "index_topk.hip", "attend_body.hpp", "attend.hip", "store.hip", "rows.hip", "rows_body.hpp", "quant.hpp",
-    "fp4.hpp", "launch.hpp")]
+    "fp4.hpp", "launch.hpp", "store_body.hpp")]
 
 
 def traffic_file(workload):
@@ -130,8 +131,13 @@ def step_bytes(cfg, lay, ids_np, G):
     # m3s_index_topk_attend: the index call's bytes, the distinct selected K/V, the main
     # query, the fp32 output and the ids it writes
     fused_call = index_call + attend + R * G * 256 + R * G * 128 * 4 + R * cfg.topk * 4
+    # m3s_decode_step: the fused call, the store, and the row map (cu_q and seq_lens in;
+    # row_req, row_len and the block prefix out)
+    B = len(seq)
+    step_call = fused_call + store + (2 * B + 1) * 4 + 2 * R * 4 + (B + 1) * 4
     return {"index": index, "attend": attend, "store": store, "other": other,
-            "total": index + attend + other, "index_call": index_call, "fused_call": fused_call}
+            "total": index + attend + other, "index_call": index_call, "fused_call": fused_call,
+            "step_call": step_call}
 
 
 def cpu_baseline(cfg, case, nreq, log_fn):
@@ -178,6 +184,7 @@ COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many 
 
 
 FRONT_KERNELS = ("store_rows_kernel", "store_kernel", "decode_rows_kernel", "prefill_rows_kernel")
+STEP_OPENERS = FRONT_KERNELS + ("step_scan_kernel",)   # the first kernel of a step, in each call mode
 
 
 def kernel_short(name):
@@ -204,12 +211,13 @@ def _base(short):
 
 def step_sequences(dispatches):
     """dispatches: [(dispatch order, short kernel name, payload)] of the library's kernels.
-    Splits them at each front kernel (the store that opens a step) and returns the most
+    Splits them at each kernel that opens a step (the store, or the decode step's first
+    kernel) and returns the most
     common kernel-name sequence and the list of runs that have it."""
     dispatches = sorted(dispatches, key=lambda t: t[0])
     runs, cur = [], None
     for d in dispatches:
-        if _base(d[1]) in FRONT_KERNELS and (cur is None or _base(cur[-1][1]) not in FRONT_KERNELS):
+        if _base(d[1]) in STEP_OPENERS and (cur is None or _base(cur[-1][1]) not in STEP_OPENERS):
             if cur:
                 runs.append(cur)
             cur = [d]
@@ -345,8 +353,9 @@ def ingest_trace(trace_csv, config):
     log(json.dumps(rec, indent=1))
 
 
-def load_record(path, workload):
-    """A committed profile record, if it was taken on the current kernel code."""
+def load_record(path, workload, calls=None):
+    """A committed profile record, if it was taken on the current kernel code (and, given
+    calls, in that call mode: a decode step record opens with the step's scan kernel)."""
     if not os.path.exists(path):
         return None
     try:
@@ -356,6 +365,10 @@ def load_record(path, workload):
         return None
     if rec.get("source_sha") != source_sha(KERNEL_SOURCES) or rec.get("workload") != workload:
         return None
+    if calls is not None:
+        first = _base(rec["step_kernels"][0]["kernel"]) if rec.get("step_kernels") else ""
+        if (first == "step_scan_kernel") != (calls == "step"):
+            return None
     return rec
 
 
@@ -414,9 +427,12 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
-    ap.add_argument("--separate", action="store_true",
-                    help="one call per stage: m3s_store, m3s_decode_rows, m3s_index_topk, m3s_sparse_attend "
-                         "(default: m3s_store_and_rows and m3s_index_topk_attend)")
+    ap.add_argument("--calls", choices=("step", "two", "separate"), default="step",
+                    help="step: one m3s_decode_step call (decode workloads; a prefill chunk runs 'two'); "
+                         "two: m3s_store_and_rows (decode) or m3s_store + m3s_prefill_rows (prefill), then "
+                         "m3s_index_topk_attend; separate: m3s_store, the row map, m3s_index_topk, "
+                         "m3s_sparse_attend")
+    ap.add_argument("--separate", action="store_true", help="same as --calls separate")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB float32 copy kernel (torch.neg) whose HBM bytes are known, "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -508,10 +524,20 @@ def main():
     ws_a = m3s.attend_workspace(rows, lay.max_blocks, cfg.topk, G, dev)
 
     ws_f = m3s.index_attend_workspace(rows, lay.max_blocks, cfg.topk, G, dev)
-    fused_front = not prefill and not args.separate
-    fused_attend = not args.separate
+    calls = "separate" if args.separate else args.calls
+    if calls == "step" and prefill:
+        calls = "two"
+    fused_front = not prefill and calls != "separate"
+    fused_attend = calls != "separate"
+
+    def decode_step(c):
+        m3s.m3s_decode_step(c, k_new, v_new, i_new, s_new, cu_q, seq, R, row_req, row_len, req_blk, case.q_idx,
+                            case.q, bt, lay.max_blocks, cfg.topk, cfg.sm_scale, 0, ids, out, ws_f, status)
 
     def run_step(c):
+        if calls == "step":
+            decode_step(c)
+            return
         if fused_front:
             m3s.m3s_store_and_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, row_req, row_len, req_blk, status)
         else:
@@ -654,7 +680,8 @@ def main():
         stages += [("qknorm_rope_store", lambda c: m3s.m3s_qknorm_rope_store(
                        pc, p_q, *p_rows, p_w, 1e-6, p_pos, p_cs, p_slots, q_out=p_out[0], idx_q_out=p_out[1],
                        dev_status=status)),
-                   ("store", lambda c: m3s.m3s_store(pc, k_new, v_new, i_new, p_slots, status))]
+                   ("store", lambda c: m3s.m3s_store(pc, k_new, v_new, i_new, p_slots, status)),
+                   ("decode_step", decode_step)]
     reps = max(1, args.stage_reps)
     stage_ms = []
     for _, fn in stages:
@@ -685,8 +712,9 @@ def main():
     log(f"[bench] algorithmic bytes/step: index {by['index'] / 1e6:.2f} MB, attend {by['attend'] / 1e6:.2f} MB, "
         f"other {by['other'] / 1e6:.2f} MB, total {by['total'] / 1e6:.2f} MB -> {gbs_step:.0f} GB/s")
     roofline = roofline_index = kernel_split = None
-    trace = load_record(trace_file(cfg.name), cfg.name)
-    traffic = load_record(traffic_file(cfg.name), cfg.name)
+    trace = load_record(trace_file(cfg.name), cfg.name, calls)
+    traffic = load_record(traffic_file(cfg.name), cfg.name, calls)
+    stage_of = {nm: v for (nm, _), v in zip(stages, stage_ms)}
     if stage_ms:
         names = [nm for nm, _ in stages]
         log("[bench] stages (us, each stage launched back to back): " +
@@ -696,14 +724,26 @@ def main():
         call_kernels = None
         if trace:
             call_kernels = [k["kernel"] for k in trace["step_kernels"] if _base(k["kernel"]) not in FRONT_KERNELS]
-        # the call the step runs: m3s_index_topk_attend, its algorithmic bytes over its
-        # launch time (HIP events on its stream)
-        ach = by["fused_call"] / t_fused / 1e9
-        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": traffic["fused_call_bytes"] if traffic else None,
-                    "kernel": "m3s_index_topk_attend" + (f" ({', '.join(call_kernels)})" if call_kernels else ""),
-                    "launch_us": round(stage_ms[3] * 1e3, 2), "bytes_per_launch": by["fused_call"]}
+        if calls == "step":
+            # the call the step runs: m3s_decode_step, the whole path's algorithmic bytes
+            # over its launch time (HIP events on its stream)
+            t_call = stage_of["decode_step"] / 1e3
+            ach = by["step_call"] / t_call / 1e9
+            step_kernels = [k["kernel"] for k in trace["step_kernels"]] if trace else None
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 4),
+                        "traffic": traffic["step_bytes"] if traffic else None,
+                        "kernel": "m3s_decode_step" + (f" ({', '.join(step_kernels)})" if step_kernels else ""),
+                        "launch_us": round(t_call * 1e6, 2), "bytes_per_launch": by["step_call"]}
+        else:
+            # the call the step runs: m3s_index_topk_attend, its algorithmic bytes over its
+            # launch time (HIP events on its stream)
+            ach = by["fused_call"] / t_fused / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(ach / HBM_PEAK_GBS, 4),
+                        "traffic": traffic["fused_call_bytes"] if traffic else None,
+                        "kernel": "m3s_index_topk_attend" + (f" ({', '.join(call_kernels)})" if call_kernels else ""),
+                        "launch_us": round(stage_ms[3] * 1e3, 2), "bytes_per_launch": by["fused_call"]}
         ach_i = by["index_call"] / t_idx / 1e9
         roofline_index = {"kernel": "m3s_index_topk (scan + select)", "achieved": round(ach_i, 1),
                           "frac": round(ach_i / HBM_PEAK_GBS, 4), "launch_us": round(stage_ms[1] * 1e3, 2),
@@ -723,7 +763,7 @@ def main():
     if trace:
         # per-kernel durations of the step from the committed kernel trace (taken on the
         # current kernel code), with the algorithmic bytes of the kernels that have them
-        kb = {"index_scan_kernel": by["index_call"]}
+        kb = {"index_scan_kernel": by["index_call"], "step_scan_kernel": by["index_call"] + by["store"]}
         kernel_split = []
         for k in trace["step_kernels"]:
             b = kb.get(_base(k["kernel"]))
@@ -756,8 +796,11 @@ def main():
         "config": {"workload": cfg.name, "requests": len(lay.seq_lens), "rows_per_request": cfg.q_len,
                    "context": [int(x) for x in sorted(set(lay.seq_lens.tolist()))][:4],
                    "heads_per_kv_head": G, "topk": cfg.topk, "cache_format": cfg.fmt, "layers_cycled": NL,
-                   "front": "m3s_store_and_rows" if fused_front else "separate store and row-map calls",
-                   "topk_attend": "m3s_index_topk_attend" if fused_attend else "separate m3s_index_topk, m3s_sparse_attend"},
+                   "calls": {"step": "m3s_decode_step",
+                             "two": ("m3s_store + m3s_prefill_rows" if prefill else "m3s_store_and_rows") +
+                                    ", m3s_index_topk_attend",
+                             "separate": "m3s_store, " + ("m3s_prefill_rows" if prefill else "m3s_decode_rows") +
+                                         ", m3s_index_topk, m3s_sparse_attend"}[calls]},
         "hbm_gbs_step": round(gbs_step, 1),
         "steps_per_graph": GL,
         "us_per_step_one_graph_each": round(ms_single * 1e3, 2),

@@ -7,7 +7,8 @@ the path runs in the library's HIP kernels. Loading fails loudly when the
 library is missing: there is no fallback.
 
 Functions carry the C names: m3s_store, m3s_decode_rows, m3s_store_and_rows, m3s_prefill_rows,
-m3s_qknorm_rope_store, m3s_index_topk, m3s_sparse_attend, m3s_index_topk_attend, m3s_workspace_bytes,
+m3s_qknorm_rope_store, m3s_index_topk, m3s_sparse_attend, m3s_index_topk_attend, m3s_decode_step,
+m3s_workspace_bytes,
 m3s_read_device_status, m3s_status_string, m3s_version.
 """
 from __future__ import annotations
@@ -30,13 +31,13 @@ TOPK_TIE_HIGH_ID = 1
 DEV_BITS = {
     "BAD_SLOT": 1 << 0, "BAD_ROWS": 1 << 1, "BAD_LENGTH": 1 << 2, "BAD_PAGE": 1 << 3,
     "BAD_BLOCK_ID": 1 << 4, "INEXACT": 1 << 5, "BAND_OVERFLOW": 1 << 6, "BAD_POSITION": 1 << 7,
-    "RANGE": 1 << 8,
+    "RANGE": 1 << 8, "STEP_SLOT": 1 << 9,
 }
 
 EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_qknorm_rope_store",
            "m3s_index_topk", "m3s_sparse_attend", "m3s_index_topk_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version",
-           "m3s_probe_page_reads", "m3s_index_topk_attend_noalloc")
+           "m3s_probe_page_reads", "m3s_index_topk_attend_noalloc", "m3s_decode_step")
 NOALLOC_SCRATCH_BYTES = 32 << 20
 MAX_GROUPS = 4096
 GROUP_ROWS = 64
@@ -97,6 +98,8 @@ def load(path: str | None = None):
         "m3s_probe_page_reads": (I32, [V, V, V, I32, I32, V, I32, V]),
         "m3s_index_topk_attend_noalloc": (I32, [V, V, I64, V, I64, I64, I32, V, I32, I32, V, I32, I32, I32, I32,
                                                 F32, V, V, V, V]),
+        "m3s_decode_step": (I32, [V, V, V, V, I64, V, V, V, I32, I32, V, V, V, V, I64, V, I64, I64, I32, V, I32,
+                                  I32, I32, I32, I32, I32, F32, V, V, V, SZ, V, V]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -473,6 +476,58 @@ def m3s_index_topk_attend_noalloc(cache: Cache, q_idx, q, block_table, max_block
                                               _ptr(topk_ids), _ptr(out), _ptr(dev_status), _stream(stream))
     _check("m3s_index_topk_attend_noalloc", st)
     return topk_ids, out
+
+
+def m3s_decode_step(cache: Cache, k, v, idx, slot_mapping, cu_q, seq_lens, num_rows: int, row_req, row_len,
+                    req_blk, q_idx, q, block_table, max_blocks: int, topk: int, sm_scale: float, flags: int = 0,
+                    topk_ids=None, out=None, workspace=None, dev_status=None, stream=None, init_blocks: int = 0,
+                    local_blocks: int = 0):
+    """One decode step: m3s_store_and_rows then m3s_index_topk_attend, with the store,
+    the row map and the index scan in one launch. The step's tokens are its rows
+    (k, v, idx and slot_mapping have num_rows rows). Returns (rows, topk_ids, out)."""
+    torch = _torch()
+    T = num_rows
+    stride = None
+    for name, t in (("k", k), ("v", v), ("idx", idx)):
+        if t is not None:
+            _need(t, name, torch.bfloat16)
+            stride = t.stride(0) if stride is None else stride
+            if t.shape[0] != T or t.stride(0) != stride or t.stride(1) != 1 or t.shape[1] < HEAD_DIM:
+                raise ValueError(f"{name}: rows must share [num_rows, >=128] shape and row stride")
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    _need(cu_q, "cu_q", torch.int32)
+    _need(seq_lens, "seq_lens", torch.int32)
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(q, "q", torch.bfloat16)
+    _need(block_table, "block_table", torch.int32)
+    B = seq_lens.numel()
+    if slot_mapping.numel() != T or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 [num_rows]")
+    if cu_q.numel() != B + 1:
+        raise ValueError("cu_q must have num_reqs + 1 entries")
+    if q_idx.dim() != 2 or q_idx.stride(1) != 1 or q_idx.shape[1] < HEAD_DIM:
+        raise ValueError("q_idx must be [R, >=128] with unit inner stride")
+    if q.dim() != 3 or q.stride(2) != 1 or q.shape[2] < HEAD_DIM:
+        raise ValueError("q must be [R, G, >=128] with unit inner stride")
+    if block_table.dim() != 2 or block_table.stride(1) != 1:
+        raise ValueError("block_table must be [B, stride] with unit inner stride")
+    G = q.shape[1]
+    dev = q.device
+    rows = Rows(cu_q, None, req_blk, row_req, row_len, B, num_rows)
+    if topk_ids is None:
+        topk_ids = torch.empty((num_rows, topk), dtype=torch.int32, device=dev)
+    if out is None:
+        out = torch.empty((num_rows, G, HEAD_DIM), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = index_attend_workspace(rows, max_blocks, topk, G, dev)
+    st = load().m3s_decode_step(cache.ref(), _ptr(k), _ptr(v), _ptr(idx), stride or HEAD_DIM, _ptr(slot_mapping),
+                                _ptr(cu_q), _ptr(seq_lens), B, num_rows, _ptr(row_req), _ptr(row_len), _ptr(req_blk),
+                                _ptr(q_idx), q_idx.stride(0), _ptr(q), q.stride(0), q.stride(1), G,
+                                _ptr(block_table), block_table.stride(0), max_blocks, topk, flags, init_blocks,
+                                local_blocks, float(sm_scale), _ptr(topk_ids), _ptr(out), _ptr(workspace),
+                                workspace.numel(), _ptr(dev_status), _stream(stream))
+    _check("m3s_decode_step", st)
+    return rows, topk_ids, out
 
 
 def m3s_read_device_status(dev_status, stream=None) -> int:

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libm3s.so")
 
 HIP_SOURCES = ["store.hip", "producer.hip", "rows.hip", "index_topk.hip", "attend.hip", "probe.hip", "scratch.hip"]
 HOST_SOURCES = ["api.cpp"]
-HEADERS = ["fp4.hpp", "launch.hpp", "quant.hpp", "rows_body.hpp"]
+HEADERS = ["fp4.hpp", "launch.hpp", "quant.hpp", "rows_body.hpp", "store_body.hpp"]
 
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]

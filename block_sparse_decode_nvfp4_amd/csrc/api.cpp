@@ -317,6 +317,7 @@ m3s_status index_args(IndexArgs& a, const m3s_cache* cache, const uint16_t* q_id
   a.row_req = rows->row_req;
   a.row_len = rows->row_len;
   a.req_blk = rows->grp_blk;
+  a.seq_lens = nullptr;
   a.num_reqs = rows->num_groups;
   a.num_rows = rows->num_rows;
   a.topk = topk;
@@ -492,6 +493,51 @@ m3s_status m3s_index_topk_attend_noalloc(const m3s_cache* cache, const uint16_t*
   return index_topk_attend_impl(cache, q_idx, q_idx_stride, q, q_row_stride, q_head_stride, num_heads, block_table,
                                 bt_stride, max_blocks, rows, topk, flags, init_blocks, local_blocks, sm_scale,
                                 topk_ids, out, ws, M3S_NOALLOC_SCRATCH_BYTES, dev_status, stream);
+}
+
+m3s_status m3s_decode_step(const m3s_cache* cache, const uint16_t* k, const uint16_t* v, const uint16_t* idx_k,
+                           int64_t row_stride, const int32_t* slot_mapping, const int32_t* cu_q,
+                           const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows, int32_t* row_req,
+                           int32_t* row_len, int32_t* req_blk, const uint16_t* q_idx, int64_t q_idx_stride,
+                           const uint16_t* q, int64_t q_row_stride, int64_t q_head_stride, int32_t num_heads,
+                           const int32_t* block_table, int32_t bt_stride, int32_t max_blocks, int32_t topk,
+                           int32_t flags, int32_t init_blocks, int32_t local_blocks, float sm_scale,
+                           int32_t* topk_ids, float* out, void* workspace, size_t workspace_bytes,
+                           uint32_t* dev_status, hipStream_t stream) {
+  StoreArgs s;
+  m3s_status st = store_args(s, cache, k, v, idx_k, row_stride, slot_mapping, num_rows, dev_status);
+  if (st != M3S_OK) return st;
+  RowsArgs r;
+  st = rows_args(r, cu_q, seq_lens, num_reqs, num_rows, row_req, row_len, req_blk, dev_status);
+  if (st != M3S_OK) return st;
+  m3s_rows rows;
+  rows.grp_row = cu_q;
+  rows.grp_req = nullptr;
+  rows.grp_blk = req_blk;
+  rows.row_req = row_req;
+  rows.row_len = row_len;
+  rows.num_groups = num_reqs;
+  rows.num_rows = num_rows;
+  if (max_blocks < 0) return M3S_ERR_INVALID_ARG;
+  const size_t ni = align256(index_ws_bytes(num_rows, max_blocks));
+  if (workspace_bytes < ni) return M3S_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  IndexArgs ia;
+  st = index_args(ia, cache, q_idx, q_idx_stride, block_table, bt_stride, max_blocks, &rows, topk, flags,
+                  init_blocks, local_blocks, topk_ids, ws, ni, dev_status);
+  if (st != M3S_OK) return st;
+  AttendArgs aa;
+  st = attend_args(aa, cache, q, q_row_stride, q_head_stride, num_heads, block_table, bt_stride, max_blocks, &rows,
+                   topk_ids, topk, sm_scale, out, ws ? ws + ni : nullptr, workspace_bytes - ni, dev_status);
+  if (st != M3S_OK) return st;
+  const size_t np = fused_ws_pages_offset(num_rows, max_blocks, topk);
+  if (num_rows > 0 && workspace_bytes < np + align256((size_t)num_rows * topk * sizeof(int32_t)))
+    return M3S_ERR_WORKSPACE;
+  ia.sel_pages = num_rows > 0 ? reinterpret_cast<int32_t*>(ws + np) : nullptr;
+  aa.sel_pages = ia.sel_pages;
+  ia.seq_lens = seq_lens;
+  if (ia.scan_grid == 0) ia.scan_grid = scan_grid();
+  return from_hip(launch_decode_step(ia, aa, s, r, stream));
 }
 
 m3s_status m3s_read_device_status(const uint32_t* dev_status, uint32_t* out, hipStream_t stream) {

@@ -41,6 +41,8 @@
 #include "fp4.hpp"
 #include "launch.hpp"
 #include "attend_body.hpp"
+#include "rows_body.hpp"
+#include "store_body.hpp"
 
 namespace m3s {
 
@@ -74,6 +76,9 @@ struct PageBuf {
 template <int FMT>
 __device__ __forceinline__ void load_page(PageBuf& p, const IndexArgs& a, int page, int n, int G) {
   constexpr int SB = FMT == 1 ? 8 : 4;
+  // the page is the wave's (uniform): its base goes to scalar registers, the loads take
+  // it as their scalar base with one lane offset each
+  page = __builtin_amdgcn_readfirstlane(page);
   const uint8_t* pay = a.idx_data + (int64_t)page * (kPage * kPayload);
   const uint8_t* scb = a.idx_scale + (int64_t)page * (kPage * SB);
 #pragma unroll
@@ -242,8 +247,16 @@ __device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int
   q.b = b;
   q.r0 = g0 + 16 * k;
   q.ql = min(max(a.cu_q[b + 1] - q.r0, 0), 16);
-  q.min_len = q.ql > 0 ? a.row_len[q.r0] : 0x7FFFFFFF;
-  q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
+  if (a.seq_lens) {
+    // decode step: row r of request b sees seq_len - q_len + 1 + (r - cu_q[b]) tokens
+    // (the row map is written by the same launch, so it is derived here)
+    const int base = a.seq_lens[b] - (a.cu_q[b + 1] - g0) + 1 - g0;
+    q.min_len = q.ql > 0 ? base + q.r0 : 0x7FFFFFFF;
+    q.len_n = n < q.ql ? base + q.r0 + n : 0;
+  } else {
+    q.min_len = q.ql > 0 ? a.row_len[q.r0] : 0x7FFFFFFF;
+    q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
+  }
   build_query<FMT>(q, a, n < q.ql ? q.r0 + n : -1, n, G);
 }
 
@@ -421,8 +434,69 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
 // scores them in H = 2 passes of NT = 2 tiles, a (group, block, half) unit each.
 constexpr int kScanChunk = 1024;  // units staged in LDS at a time
 
-template <int FMT, int NT, int WAVES, int H>
-__global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
+// ---------------------------------------------------------------------------
+// the decode step's scan (m3s_decode_step): store, row map and scan in one launch
+// ---------------------------------------------------------------------------
+// Inclusive prefix sum over the 64 lanes of a wave (six lane-xor exchanges, no LDS):
+// after the exchange with lane ^ M, tot is the sum over the lane's aligned group of 2M
+// lanes, and a lane in the upper half of that group adds the lower half's sum.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  const int lane = threadIdx.x & 63;
+  int tot = x;
+  int t;
+  t = lane_xor<1>(tot);
+  if (lane & 1) x += t;
+  tot += t;
+  t = lane_xor<2>(tot);
+  if (lane & 2) x += t;
+  tot += t;
+  t = lane_xor<4>(tot);
+  if (lane & 4) x += t;
+  tot += t;
+  t = lane_xor<8>(tot);
+  if (lane & 8) x += t;
+  tot += t;
+  t = lane_xor<16>(tot);
+  if (lane & 16) x += t;
+  tot += t;
+  t = lane_xor<32>(tot);
+  if (lane & 32) x += t;
+  return x;
+}
+
+// A request the decode row map accepts: its rows lie in [0, num_rows), q_len in [1, 16],
+// seq_len >= q_len.
+__device__ __forceinline__ bool step_request_ok(int q0, int q1, int sl, int num_rows) {
+  const int ql = q1 - q0;
+  return q0 >= 0 && q1 <= num_rows && ql >= 1 && ql <= kMaxQLen && sl >= ql;
+}
+
+// Wave 0: s_blk[b] = exclusive prefix over the requests of each accepted request's
+// blocks with no new token, floor((seq_len - q_len) / 128) (0 for the others). The
+// decode step's scan takes these blocks; the tail workgroups the rest.
+__device__ __forceinline__ void step_prefix_old(const IndexArgs& a, int* s_blk) {
+  const int lane = threadIdx.x & 63;
+  const int B = a.num_reqs;
+  int carry = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int b = base + lane;
+    int nb = 0;
+    if (b < B) {
+      const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
+      if (step_request_ok(q0, q1, sl, a.num_rows)) nb = (sl - (q1 - q0)) / kPage;
+    }
+    const int x = wave_incl_sum(nb);
+    if (b < B) s_blk[b] = carry + x - nb;
+    carry += __builtin_amdgcn_readlane(x, 63);
+  }
+  if (lane == 0) s_blk[B] = carry;
+}
+
+// STEP: the decode step's scan (NT = H = 1): its units are each accepted request's
+// blocks with no new token (step_prefix_old), and the rows' causal lengths come from
+// seq_lens (load_query), since the row map is written by the same launch.
+template <int FMT, int NT, int WAVES, int H, bool STEP>
+__device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
   constexpr int kScanWaves = WAVES;
   __shared__ int s_blk[M3S_MAX_REQS_INTERNAL + 1];
   __shared__ int s_unit[kScanChunk];  // request * kMaxBlocks + block; -1: not scored
@@ -431,11 +505,16 @@ __global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, G = lane >> 4;
   const int B = a.num_reqs;
-  for (int i = tid; i <= B; i += kScanWaves * 64) s_blk[i] = a.req_blk[i];
+  if constexpr (STEP) {
+    static_assert(NT == 1 && H == 1, "the decode step's scan");
+    if (tid < 64) step_prefix_old(a, s_blk);
+  } else {
+    for (int i = tid; i <= B; i += kScanWaves * 64) s_blk[i] = a.req_blk[i];
+  }
   __syncthreads();
   const int64_t total = (int64_t)s_blk[B] * H;
-  const int64_t w0 = (int64_t)blockIdx.x * total / gridDim.x;
-  const int64_t w1 = (int64_t)(blockIdx.x + 1) * total / gridDim.x;
+  const int64_t w0 = (int64_t)wg * total / nwg;
+  const int64_t w1 = (int64_t)(wg + 1) * total / nwg;
 
   auto req_of = [&](int64_t u) {  // largest b with s_blk[b] <= u
     int lo = 0, hi = B - 1;
@@ -449,33 +528,6 @@ __global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
     int v = 0;
     if (lane == 0) v = atomicAdd(&s_ctr, 1);
     return __builtin_amdgcn_readlane(v, 0);
-  };
-
-  QueryTile qt[NT];
-  int qb = -1;  // (work group, pass) whose query tiles qt holds
-  PageBuf pa;
-  auto process = [&](const PageBuf& buf, int i) {
-    const int key = s_unit[i];
-    if (key < 0) return;
-    const int bh = key / kMaxBlocks, j = key - bh * kMaxBlocks;
-    if (bh != qb) {
-      qb = bh;
-#pragma unroll
-      for (int k = 0; k < NT; ++k) load_query<FMT>(qt[k], a, bh / H, NT * (bh % H) + k, n, G);
-    }
-    if (s_page[i] >= 0) {
-      if constexpr (NT == 1) score_page<FMT>(buf, qt[0], a, j, n, G);
-      else score_page_n<FMT, NT>(buf, qt, a, j, n, G);
-    } else if (G == 0) {
-#pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        if (n < qt[k].ql) {
-          const int64_t o = (int64_t)(qt[k].r0 + n) * a.max_blocks + j;
-          a.ws_score[o] = -INFINITY;
-          a.ws_bound[o] = 0.f;
-        }
-      }
-    }
   };
 
   for (int64_t c0 = w0; c0 < w1; c0 += kScanChunk) {  // uniform over the workgroup
@@ -504,16 +556,42 @@ __global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
     }
     if (tid == 0) s_ctr = 0;
     __syncthreads();
+    QueryTile qt[NT];
+    int qb = -1;  // (work group, pass) whose query tiles qt holds
+    auto process = [&](const PageBuf& buf, int key, int pg) {
+      if (key < 0) return;
+      const int bh = key / kMaxBlocks, j = key - bh * kMaxBlocks;
+      if (bh != qb) {
+        qb = bh;
+#pragma unroll
+        for (int k = 0; k < NT; ++k) load_query<FMT>(qt[k], a, bh / H, NT * (bh % H) + k, n, G);
+      }
+      if (pg >= 0) {
+        if constexpr (NT == 1) score_page<FMT>(buf, qt[0], a, j, n, G);
+        else score_page_n<FMT, NT>(buf, qt, a, j, n, G);
+      } else if (G == 0) {
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+          if (n < qt[k].ql) {
+            const int64_t o = (int64_t)(qt[k].r0 + n) * a.max_blocks + j;
+            a.ws_score[o] = -INFINITY;
+            a.ws_bound[o] = 0.f;
+          }
+        }
+      }
+    };
     // one page in flight per wave; the other waves of the SIMD cover its latency
     // (measured: for the prefill variant a second page in flight per wave was
     // slower, its time goes to the scoring itself)
     while (true) {
-      const int i0 = claim();
-      if (i0 >= cnt) break;
+      const int c = claim();
+      if (c >= cnt) break;
+      // uniform over the wave (read from LDS at a uniform index)
+      const int key = __builtin_amdgcn_readfirstlane(s_unit[c]);
+      const int pg = __builtin_amdgcn_readfirstlane(s_page[c]);
       if constexpr (NT > 1) {
         // a new group's query tiles are built before its page is loaded, so the
         // page registers are not live across the build
-        const int key = s_unit[i0];
         const int bh = key / kMaxBlocks;
         if (key >= 0 && bh != qb) {
           qb = bh;
@@ -524,10 +602,127 @@ __global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
           }
         }
       }
-      if (s_page[i0] >= 0) load_page<FMT>(pa, a, s_page[i0], n, G);
-      process(pa, i0);
+      PageBuf pa;  // per unit: no page registers live across iterations
+      if (pg >= 0) load_page<FMT>(pa, a, pg, n, G);
+      process(pa, key, pg);
     }
     __syncthreads();  // the chunk's LDS tables are rewritten next
+  }
+}
+
+template <int FMT, int NT, int WAVES, int H>
+__global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
+  scan_body<FMT, NT, WAVES, H, false>(a, blockIdx.x, gridDim.x);
+}
+
+// Tail workgroup t of the decode step kernel: requests [b0, b1), at most four (the
+// launcher's split). It stores the step's new rows (every token in its share
+// [t T / ntail, (t + 1) T / ntail) of the T tokens, and again the tokens of its own
+// requests, so that those are in the planes before it reads them: writing the same
+// bytes twice is harmless), waits for its stores, then scores each of its requests'
+// blocks that hold a new token against the request's rows with the scan's
+// arithmetic, one block per wave (a request's q_len <= 16 new tokens touch at most
+// two blocks, so at most 8 of the 16 waves score). No other workgroup reads those
+// pages in this launch. Every load that does not need the stores (the rows to
+// store, the slots, the block-table entries, the queries) is issued before the
+// first wait.
+template <int FMT>
+__device__ __forceinline__ void tail_body(const IndexArgs& a, const StoreArgs& s, int t, int ntail) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, G = lane >> 4, l16 = tid & 15;
+  const int B = a.num_reqs;
+  const int b0 = (int)((int64_t)t * B / ntail), b1 = (int)((int64_t)(t + 1) * B / ntail);
+  // the own requests' tokens lie in [lo, hi) (all rows of an accepted request are in
+  // [0, num_rows), and num_tokens = num_rows); the wave's tail unit (ub, uj)
+  int lo = 0x7FFFFFFF, hi = 0, nu = 0, ub = -1, uj = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
+    if (!step_request_ok(q0, q1, sl, a.num_rows)) continue;
+    lo = min(lo, q0);
+    hi = max(hi, q1);
+    const int j_lo = (sl - (q1 - q0)) / kPage, j_hi = (sl + kPage - 1) / kPage;
+    if (w >= nu && w < nu + (j_hi - j_lo)) {
+      ub = b;
+      uj = j_lo + (w - nu);
+    }
+    nu += j_hi - j_lo;
+  }
+  const int64_t T = s.num_tokens;
+  const int64_t sh0 = (int64_t)t * T / ntail * 3, sh1 = (int64_t)(t + 1) * T / ntail * 3;
+  const int64_t ow0 = (int64_t)lo * 3, ow1 = min((int64_t)hi, T) * 3;
+  // first 192 rows of the share and of the own tokens: loads in flight together
+  StoreLoad sh[3], ow[3];
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const int64_t r1 = sh0 + 64 * p + (tid >> 4), r2 = ow0 + 64 * p + (tid >> 4);
+    store_issue(s, r1 < sh1 ? r1 : -1, l16, sh[p]);
+    store_issue(s, r2 < ow1 ? r2 : -1, l16, ow[p]);
+  }
+  // decode convention, lanes (k, i) of wave 0: token i of request b0 + k goes to
+  // position seq_len - q_len + i of that request's block table
+  int chk_slot = -1, chk_want = -1;
+  if (tid < 64 && b0 + (tid >> 4) < b1) {
+    const int b = b0 + (tid >> 4), i = tid & 15;
+    const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
+    const int ql = q1 - q0;
+    if (step_request_ok(q0, q1, sl, a.num_rows) && i < ql && q0 + i < T) {
+      const int pos = sl - ql + i, j = pos / kPage;
+      const int pg = j < a.max_blocks ? a.block_table[(int64_t)b * a.bt_stride + j] : -1;
+      chk_slot = s.slots[q0 + i];
+      if (pg >= 0 && pg < a.num_pages) chk_want = pg * kPage + pos % kPage;
+    }
+  }
+  // the wave's unit: its page entry and its query tile
+  int pg = -1;
+  QueryTile qt;
+  if (ub >= 0 && uj < a.max_blocks) {
+    pg = a.block_table[(int64_t)ub * a.bt_stride + uj];
+    load_query<FMT>(qt, a, ub, 0, n, G);
+  }
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    store_commit<FMT>(s, l16, sh[p]);
+    store_commit<FMT>(s, l16, ow[p]);
+  }
+  // rows past the first 192 of either range (not met by a well-formed step)
+  for (int64_t rr = sh0 + 192 + (tid >> 4); rr < sh1; rr += 64) store_row<FMT>(s, rr, l16);
+  for (int64_t rr = ow0 + 192 + (tid >> 4); rr < ow1; rr += 64) store_row<FMT>(s, rr, l16);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have landed (vmcnt counts stores)
+  __syncthreads();                // ... and every wave's, before any page read
+  if (chk_want >= 0 && chk_slot != chk_want) set_status(a.status, kDevStepSlot);
+  if (ub < 0) return;
+  if (uj >= a.max_blocks) {
+    if (lane == 0) set_status(a.status, kDevBadLength);
+    return;
+  }
+  if (pg < 0 || pg >= a.num_pages) {
+    if (lane == 0) set_status(a.status, kDevBadPage);
+    if (G == 0 && n < qt.ql) {
+      const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + uj;
+      a.ws_score[o] = -INFINITY;
+      a.ws_bound[o] = 0.f;
+    }
+    return;
+  }
+  PageBuf pa;
+  load_page<FMT>(pa, a, pg, n, G);
+  score_page<FMT>(pa, qt, a, uj, n, G);
+}
+
+// The decode step's first kernel: workgroup 0 builds the row map (m3s_decode_rows),
+// workgroups 1 .. ntail store the step's new rows and score the blocks that hold them
+// (tail_body), and the rest scan every other causal block (scan_body with STEP). The
+// three are independent within the launch, so the store and the row map cost no
+// launch of their own.
+template <int FMT>
+__global__ __launch_bounds__(1024) void step_scan_kernel(IndexArgs a, StoreArgs s, RowsArgs r, int ntail) {
+  if (blockIdx.x == 0) {
+    __shared__ int s_scan[16];
+    decode_rows_body<1024>(r, s_scan);
+  } else if ((int)blockIdx.x <= ntail) {
+    tail_body<FMT>(a, s, blockIdx.x - 1, ntail);
+  } else {
+    scan_body<FMT, 1, 16, 1, true>(a, blockIdx.x - 1 - ntail, gridDim.x - 1 - ntail);
   }
 }
 
@@ -1133,10 +1328,9 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream) {
   return launch_select(a, stream);
 }
 
-hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream) {
-  if (ia.num_rows == 0) return hipSuccess;
-  hipError_t e = launch_scan(ia, stream);
-  if (e != hipSuccess) return e;
+// The select and the attention of a fused call, after its scan.
+static hipError_t launch_select_attend_after_scan(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream) {
+  hipError_t e;
   const int64_t wgs = (int64_t)ia.num_rows * aa.nsplit;
   if (wgs > 2 * (int64_t)ia.scan_grid || aa.reps != 1) {
     // Many rows (prefill): every split's workgroup would repeat its row's select,
@@ -1160,6 +1354,31 @@ hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, h
   e = hipGetLastError();
   if (e != hipSuccess || aa.nsplit == 1) return e;
   return launch_attend_combine(aa, stream);
+}
+
+hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream) {
+  if (ia.num_rows == 0) return hipSuccess;
+  hipError_t e = launch_scan(ia, stream);
+  if (e != hipSuccess) return e;
+  return launch_select_attend_after_scan(ia, aa, stream);
+}
+
+hipError_t launch_decode_step(const IndexArgs& ia, const AttendArgs& aa, const StoreArgs& s, const RowsArgs& r,
+                              hipStream_t stream) {
+  // tail workgroups: at most four requests each (tail_body relies on it); the scan
+  // keeps the other CUs, fewer when there are fewer than 16 blocks per workgroup
+  const int B = ia.num_reqs;
+  const int ntail = B > 0 ? (B + 3) / 4 : (s.num_tokens > 0 ? 1 : 0);
+  int64_t nscan = (int64_t)ia.scan_grid - 1 - ntail;
+  const int64_t units_upper = (int64_t)B * ia.max_blocks;
+  if (nscan * 16 > units_upper) nscan = (units_upper + 15) / 16;
+  if (nscan < 1) nscan = 1;
+  const dim3 g((unsigned)(1 + ntail + nscan)), blk(1024);
+  if (ia.format == 1) hipLaunchKernelGGL(step_scan_kernel<1>, g, blk, 0, stream, ia, s, r, ntail);
+  else hipLaunchKernelGGL(step_scan_kernel<2>, g, blk, 0, stream, ia, s, r, ntail);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ia.num_rows == 0) return e;
+  return launch_select_attend_after_scan(ia, aa, stream);
 }
 
 }  // namespace m3s

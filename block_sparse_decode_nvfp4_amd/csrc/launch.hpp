@@ -19,6 +19,7 @@ enum : uint32_t {
   kDevBandOverflow = 1u << 6,
   kDevBadPosition = 1u << 7,
   kDevRange = 1u << 8,
+  kDevStepSlot = 1u << 9,
 };
 
 constexpr int kMaxBlocks = 8192;   // causal blocks per request
@@ -103,6 +104,9 @@ struct IndexArgs {
   const int32_t* row_req;
   const int32_t* row_len;
   const int32_t* req_blk;
+  const int32_t* seq_lens;  // decode step kernel only (else null): row lengths in closed form from
+                            // seq_lens and cu_q; the scan's units are each request's blocks with no
+                            // new token, the tail workgroups score the rest
   int32_t num_reqs;
   int32_t num_rows;
   int32_t topk;
@@ -157,6 +161,8 @@ hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);
 hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, hipStream_t stream);
 hipError_t launch_attend_combine(const AttendArgs& a, hipStream_t stream);
+hipError_t launch_decode_step(const IndexArgs& ia, const AttendArgs& aa, const StoreArgs& s, const RowsArgs& r,
+                              hipStream_t stream);
 
 // The no-allocation entry point's scratch: a static device array of this size per GPU
 // (scratch.hip); noalloc_scratch gives its device address on the current device.

@@ -10,39 +10,9 @@
 #include "launch.hpp"
 #include "quant.hpp"
 #include "rows_body.hpp"
+#include "store_body.hpp"
 
 namespace m3s {
-
-template <int FMT>
-__device__ __forceinline__ void store_body(const StoreArgs& a, int64_t block) {
-  const int lane16 = threadIdx.x & 15;
-  const int64_t rr = block * 16 + (threadIdx.x >> 4);
-  const int64_t tok = rr / 3;
-  const int ten = (int)(rr - tok * 3);
-  const uint16_t* src = ten == 0 ? a.k : (ten == 1 ? a.v : a.idx);
-  uint8_t* dd = ten == 0 ? a.k_data : (ten == 1 ? a.v_data : a.idx_data);
-  uint8_t* ds = ten == 0 ? a.k_scale : (ten == 1 ? a.v_scale : a.idx_scale);
-
-  bool live = tok < a.num_tokens && src != nullptr;
-  int32_t slot = live ? a.slots[tok] : -1;
-  live = live && slot >= 0;
-  if (live && (int64_t)slot >= (int64_t)a.num_pages * kPage) {
-    if (lane16 == 0) set_status(a.status, 1u << 0);
-    live = false;
-  }
-  u32x4 raw = {0u, 0u, 0u, 0u};
-  if (live) raw = *reinterpret_cast<const u32x4*>(src + tok * a.row_stride + 8 * lane16);
-
-  uint32_t bits[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bits[2 * i] = raw[i] & 0xFFFFu;
-    bits[2 * i + 1] = raw[i] >> 16;
-  }
-  uint32_t packed, scale_byte;
-  quantize_lane<FMT>(bits, packed, scale_byte);
-  if (live) write_lane<FMT>(dd, ds, slot, lane16, packed, scale_byte);
-}
 
 template <int FMT>
 __global__ __launch_bounds__(256) void store_kernel(StoreArgs a) {

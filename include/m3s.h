@@ -102,10 +102,13 @@ enum {
                                       approximate scores */
   M3S_DEV_BAD_POSITION = 1u << 7,  /* qknorm_rope_store: position outside [0, max_pos);
                                       that token's outputs are left unwritten */
-  M3S_DEV_RANGE = 1u << 8          /* attend: an output element was not finite in fp32 (logits
+  M3S_DEV_RANGE = 1u << 8,         /* attend: an output element was not finite in fp32 (logits
                                       or sums beyond the fp32 range; MXFP4 scale bytes 253
                                       and 254, which no store writes, decode to infinity);
                                       that element is written as 0 */
+  M3S_DEV_STEP_SLOT = 1u << 9      /* decode_step: a new token's slot is not its position in its
+                                      own request's block table; the step's results are then
+                                      not defined */
 };
 
 /* Flags of m3s_index_topk. */
@@ -395,6 +398,40 @@ m3s_status m3s_index_topk_attend_noalloc(const m3s_cache* cache, const uint16_t*
                                          int32_t max_blocks, const m3s_rows* rows, int32_t topk, int32_t flags,
                                          int32_t init_blocks, int32_t local_blocks, float sm_scale, int32_t* topk_ids,
                                          float* out, uint32_t* dev_status, hipStream_t stream);
+
+/*
+ * m3s_decode_step - one decode step of the whole path: m3s_store_and_rows (with
+ * num_tokens = num_rows: token r is row r) followed by m3s_index_topk_attend on
+ *   rows = { grp_row = cu_q, grp_req = NULL, grp_blk = req_blk, row_req, row_len,
+ *            num_groups = num_reqs, num_rows },
+ * with the store, the row map and the index scan in ONE launch ([ATOM-2744]
+ * Design, Write path: the store is launch-bound on its own). In that launch one
+ * workgroup builds the row map, and each request's blocks that hold one of its new
+ * tokens are stored and scored by the same workgroup, after its stores; every other
+ * causal block is scored by the scan workgroups, which never read a page the step
+ * writes. Arguments, validation, outputs (planes, row_req, row_len, req_blk,
+ * topk_ids, out) and status bits are those of the two calls, bit for bit, when the
+ * step follows the decode convention:
+ *   - slot_mapping[r] for row r of a request b that m3s_decode_rows accepts is
+ *     block_table[b][p / 128] * 128 + p % 128 with p = seq_lens[b] - q_len_b + (r - cu_q[b]);
+ *     a row that breaks it sets M3S_DEV_STEP_SLOT (results then undefined);
+ *   - pad rows and rows of rejected requests have slot -1, and no page the step
+ *     writes is also an older block of another request (shared prefix pages are
+ *     read only); these two are not checked.
+ * (Requests whose cu_q ranges overlap, which M3S_DEV_BAD_ROWS flags, leave the row
+ * map undefined in either form.)
+ *   workspace    as for m3s_index_topk_attend (m3s_workspace_bytes(M3S_OP_INDEX_TOPK_ATTEND, ...)).
+ */
+m3s_status m3s_decode_step(const m3s_cache* cache, const uint16_t* k, const uint16_t* v,
+                           const uint16_t* idx_k, int64_t row_stride, const int32_t* slot_mapping,
+                           const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs,
+                           int32_t num_rows, int32_t* row_req, int32_t* row_len, int32_t* req_blk,
+                           const uint16_t* q_idx, int64_t q_idx_stride, const uint16_t* q,
+                           int64_t q_row_stride, int64_t q_head_stride, int32_t num_heads,
+                           const int32_t* block_table, int32_t bt_stride, int32_t max_blocks,
+                           int32_t topk, int32_t flags, int32_t init_blocks, int32_t local_blocks,
+                           float sm_scale, int32_t* topk_ids, float* out, void* workspace,
+                           size_t workspace_bytes, uint32_t* dev_status, hipStream_t stream);
 
 /* Workspace sizing (host only, pure). */
 enum { M3S_OP_INDEX_TOPK = 1, M3S_OP_SPARSE_ATTEND = 2, M3S_OP_INDEX_TOPK_ATTEND = 3 };

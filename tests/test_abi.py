@@ -287,3 +287,31 @@ def test_index_topk_attend_noalloc_refuses_sizes_past_the_scratch(lib):
     assert f(big, mb=8192) == Wk
     assert f(None) == m3s.ERR_INVALID_ARG
     assert f(_rows(nreq=1, nrows=-1)) == m3s.ERR_INVALID_ARG
+
+
+def test_decode_step_validation(lib):
+    """The one-launch decode step validates as m3s_store_and_rows and
+    m3s_index_topk_attend do, and launches nothing here."""
+    I, U, Wk = m3s.ERR_INVALID_ARG, m3s.ERR_UNSUPPORTED, m3s.ERR_WORKSPACE
+    big = 1 << 30
+
+    def f(cache=None, k=FAKE, stride=128, slots=FAKE, cu=FAKE, seq=FAKE, B=1, R=2, rq=FAKE, rb=FAKE, qi=FAKE,
+          qis=128, q=FAKE, qrs=2048, qhs=128, G=16, bt=FAKE, bts=64, mb=64, topk=16, flags=0, sm=1.0, ids=FAKE,
+          out=FAKE, ws=FAKE, wsb=big):
+        c = _cache() if cache is None else cache
+        return lib.m3s_decode_step(ctypes.byref(c), k, None, None, stride, slots, cu, seq, B, R, rq, FAKE, rb, qi,
+                                   qis, q, qrs, qhs, G, bt, bts, mb, topk, flags, 0, 0, sm, ids, out, ws, wsb, None,
+                                   None)
+
+    # the store's checks
+    assert f(slots=None) == I and f(stride=100) == I
+    assert f(cache=_cache(page=64)) == U
+    # the row map's
+    assert f(B=-1) == I and f(B=5000) == U and f(cu=None) == I and f(rb=None) == I and f(rq=None) == I
+    # the index call's and the attention's
+    assert f(qi=None) == I and f(q=None) == I and f(ids=None) == I and f(out=None) == I
+    assert f(topk=0) == U and f(G=17) == U and f(flags=2) == I and f(sm=float("nan")) == I
+    assert f(bt=None) == I and f(bts=10) == I and f(mb=-1) == I
+    assert f(ws=None) == Wk and f(wsb=0) == Wk
+    need = m3s.m3s_workspace_bytes(m3s.OP_INDEX_TOPK_ATTEND, 2, 1, 64, 16, 16)
+    assert f(wsb=need - 1) == Wk

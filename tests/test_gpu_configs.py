@@ -1,7 +1,7 @@
 """The full step on every workload configuration: ids bit-exact and attention within 5e-3
 of the oracle on every row of every request, stored planes bit-exact on sampled requests'
-pages; and the call the bench times (m3s_index_topk_attend) equal to the separate calls
-bit for bit on every row."""
+pages; and the one-call forms (m3s_index_topk_attend, and m3s_decode_step, the call the
+bench times) equal to the separate calls bit for bit on every row."""
 import time
 
 import numpy as np
@@ -51,6 +51,21 @@ def test_config_full_step(gpu, ci):
     torch.cuda.synchronize()
     assert int(st.item()) == 0
     assert torch.equal(ids_f, step.ids) and torch.equal(out_f, step.out)
+    # the call the bench times: the whole step in m3s_decode_step (store of the new rows,
+    # which are already in the cache: the same bytes again; row map; index; attention)
+    newt = torch.as_tensor(lay.new_tokens, device=DEV)
+    R = int(lay.cu_q[-1])
+    rq, rl, rb = (torch.full((n,), -7, dtype=torch.int32, device=DEV) for n in (R, R, len(lay.seq_lens) + 1))
+    _, ids_d, out_d = gpu.m3s_decode_step(
+        step.cache, step.case.k[newt], step.case.v[newt], step.case.idx[newt],
+        torch.as_tensor(lay.new_slots, device=DEV), torch.as_tensor(lay.cu_q, device=DEV),
+        torch.as_tensor(lay.seq_lens, device=DEV), R, rq, rl, rb, step.case.q_idx, step.case.q, step.bt,
+        lay.max_blocks, cfg.topk, cfg.sm_scale, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(ids_d, step.ids) and torch.equal(out_d, step.out)
+    assert torch.equal(rq, step.rows.row_req) and torch.equal(rl, step.rows.row_len)
+    assert torch.equal(rb, step.rows.grp_blk)
     # stored planes of the sampled requests (index plane: every page; K/V: the new rows' pages)
     sb = 8 if cfg.fmt == "nvfp4" else 4
     for b in PLANE_SAMPLES[ci]:
