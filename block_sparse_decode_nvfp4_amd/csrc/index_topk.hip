@@ -76,9 +76,6 @@ struct PageBuf {
 template <int FMT>
 __device__ __forceinline__ void load_page(PageBuf& p, const IndexArgs& a, int page, int n, int G) {
   constexpr int SB = FMT == 1 ? 8 : 4;
-  // the page is the wave's (uniform): its base goes to scalar registers, the loads take
-  // it as their scalar base with one lane offset each
-  page = __builtin_amdgcn_readfirstlane(page);
   const uint8_t* pay = a.idx_data + (int64_t)page * (kPage * kPayload);
   const uint8_t* scb = a.idx_scale + (int64_t)page * (kPage * SB);
 #pragma unroll
@@ -586,7 +583,8 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
     while (true) {
       const int c = claim();
       if (c >= cnt) break;
-      // uniform over the wave (read from LDS at a uniform index)
+      // uniform over the wave (read from LDS at a uniform index): in scalar registers,
+      // the page's base is the loads' scalar base, one lane offset each
       const int key = __builtin_amdgcn_readfirstlane(s_unit[c]);
       const int pg = __builtin_amdgcn_readfirstlane(s_page[c]);
       if constexpr (NT > 1) {
