@@ -613,14 +613,16 @@ __global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
   scan_body<FMT, NT, WAVES, H, false>(a, blockIdx.x, gridDim.x);
 }
 
-// Tail workgroup t of the decode step kernel: requests [b0, b1), at most four (the
+constexpr int kTailReqs = 8;  // requests per tail workgroup (at most)
+
+// Tail workgroup t of the decode step kernel: requests [b0, b1), at most kTailReqs (the
 // launcher's split). It stores the step's new rows (every token in its share
 // [t T / ntail, (t + 1) T / ntail) of the T tokens, and again the tokens of its own
 // requests, so that those are in the planes before it reads them: writing the same
 // bytes twice is harmless), waits for its stores, then scores each of its requests'
 // blocks that hold a new token against the request's rows with the scan's
 // arithmetic, one block per wave (a request's q_len <= 16 new tokens touch at most
-// two blocks, so at most 8 of the 16 waves score). No other workgroup reads those
+// two blocks, so at most 16 units for the 16 waves). No other workgroup reads those
 // pages in this launch. Every load that does not need the stores (the rows to
 // store, the slots, the block-table entries, the queries) is issued before the
 // first wait.
@@ -656,10 +658,10 @@ __device__ __forceinline__ void tail_body(const IndexArgs& a, const StoreArgs& s
     store_issue(s, r1 < sh1 ? r1 : -1, l16, sh[p]);
     store_issue(s, r2 < ow1 ? r2 : -1, l16, ow[p]);
   }
-  // decode convention, lanes (k, i) of wave 0: token i of request b0 + k goes to
-  // position seq_len - q_len + i of that request's block table
+  // decode convention, lanes (k, i) of the first waves: token i of request b0 + k goes
+  // to position seq_len - q_len + i of that request's block table
   int chk_slot = -1, chk_want = -1;
-  if (tid < 64 && b0 + (tid >> 4) < b1) {
+  if (tid < 16 * kTailReqs && b0 + (tid >> 4) < b1) {
     const int b = b0 + (tid >> 4), i = tid & 15;
     const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
     const int ql = q1 - q0;
@@ -1363,10 +1365,13 @@ hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, h
 
 hipError_t launch_decode_step(const IndexArgs& ia, const AttendArgs& aa, const StoreArgs& s, const RowsArgs& r,
                               hipStream_t stream) {
-  // tail workgroups: at most four requests each (tail_body relies on it); the scan
-  // keeps the other CUs, fewer when there are fewer than 16 blocks per workgroup
+  // tail workgroups: at most kTailReqs requests each (tail_body relies on it), four
+  // while the batch is small (measured at 8 requests of 150K: one tail workgroup of
+  // eight outlasts the scan, the step went from 46.3 to 50.8 us); the scan keeps the
+  // other CUs, fewer when there are fewer than 16 blocks per workgroup
   const int B = ia.num_reqs;
-  const int ntail = B > 0 ? (B + 3) / 4 : (s.num_tokens > 0 ? 1 : 0);
+  const int per = B <= 32 ? 4 : kTailReqs;
+  const int ntail = B > 0 ? (B + per - 1) / per : (s.num_tokens > 0 ? 1 : 0);
   int64_t nscan = (int64_t)ia.scan_grid - 1 - ntail;
   const int64_t units_upper = (int64_t)B * ia.max_blocks;
   if (nscan * 16 > units_upper) nscan = (units_upper + 15) / 16;

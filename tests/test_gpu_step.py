@@ -146,7 +146,7 @@ def test_step_page_edges(gpu, fmt):
 
 
 def test_step_many_requests(gpu):
-    """200 requests: 50 tail workgroups, each storing a share of the step."""
+    """200 requests: 25 tail workgroups of eight requests, each storing a share of the step."""
     rng = np.random.default_rng(11)
     seq = [int(x) for x in rng.integers(40, 30_000, size=200)]
     wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=2, G=4)
