@@ -295,13 +295,13 @@ def ingest_pmc(fetch_csv, write_csv, config):
                            "copy_write_kib": round(copy_w, 1), "fetch_scale": round(f_scale, 4),
                            "write_scale": round(w_scale, 4)},
            "commands": ["cd /tmp && export TMPDIR=/tmp  # $R = repository root",
-                        *[f"timeout -s KILL 150 rocprofv3 --pmc {c} --output-format csv -d $R/gpurun_out/pmc_{d} "
-                          f"-o run -- python -u $R/bench.py --config {cfg.name} --steps 20 --warmup 2 "
-                          f"--stage-reps 10 --no-cpu --copy-calibration" for c, d in (("FETCH_SIZE", "fetch"),
-                                                                                     ("WRITE_SIZE", "write"))],
+                        *[f"timeout -s KILL 200 rocprofv3 --pmc {c} --output-format csv -d "
+                          f"$R/gpurun_out/pmc_{cfg.name}_{d} -o run -- python3 -u $R/bench.py --config {cfg.name} "
+                          f"--steps 20 --warmup 2 --stage-reps 10 --no-cpu --copy-calibration"
+                          for c, d in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write"))],
                         f"python bench.py --config {cfg.name} --ingest-pmc "
-                        f"gpurun_out/pmc_fetch/run_counter_collection.csv "
-                        f"gpurun_out/pmc_write/run_counter_collection.csv"]}
+                        f"gpurun_out/pmc_{cfg.name}_fetch/run_counter_collection.csv "
+                        f"gpurun_out/pmc_{cfg.name}_write/run_counter_collection.csv"]}
     path = traffic_file(cfg.name)
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as f:
