@@ -1,5 +1,6 @@
 """The calls are safe to capture in a HIP graph: a captured step (store + row map +
-index top-k + sparse attend, decode or prefill) and a captured fused producer store,
+index top-k + sparse attend, decode or prefill, as separate calls, with the fused index
+call, or as one m3s_decode_step call) and a captured fused producer store,
 replayed several times with eager work in between that overwrites every output,
 workspace and the step's cache slots with junk, give the eager results bit for bit on
 every replay."""
@@ -31,8 +32,11 @@ def _fill_history(m3s, fmt, lay, case):
 
 @pytest.mark.parametrize("fmt,prefill,fused", [("nvfp4", False, False), ("mxfp4", False, False),
                                                ("nvfp4", True, False), ("mxfp4", True, False),
-                                               ("nvfp4", False, True), ("mxfp4", True, True)])
+                                               ("nvfp4", False, True), ("mxfp4", True, True),
+                                               ("nvfp4", False, "step"), ("mxfp4", False, "step")])
 def test_step_graph_replays_match_eager(gpu, fmt, prefill, fused):
+    """fused: False, the four calls; True, store + row map then m3s_index_topk_attend;
+    "step": one m3s_decode_step call."""
     seq = [3000, 9000, 20000]
     ql = [200, 70, 1] if prefill else [4, 8, 1]
     G, topk = 8, 8
@@ -43,6 +47,9 @@ def test_step_graph_replays_match_eager(gpu, fmt, prefill, fused):
     cache, s_new, new_idx = _fill_history(gpu, fmt, lay, case)
     k_new, v_new, i_new = (t[new_idx].contiguous() for t in (case.k, case.v, case.idx))
     pad = lambda t: torch.cat([t, torch.zeros((3,) + tuple(t.shape[1:]), dtype=t.dtype, device=DEV)])
+    if fused == "step":  # one token per row: the pad rows' tokens are zero rows with slot -1
+        k_new, v_new, i_new = pad(k_new), pad(v_new), pad(i_new)
+    s_new_rows = torch.cat([s_new, torch.full((3,), -1, dtype=torch.int32, device=DEV)])
     q, q_idx = pad(case.q), pad(case.q_idx)
     cu_q = torch.as_tensor(lay.cu_q, device=DEV)
     seq_t = torch.as_tensor(lay.seq_lens, device=DEV)
@@ -62,6 +69,10 @@ def test_step_graph_replays_match_eager(gpu, fmt, prefill, fused):
     ws_f = gpu.index_attend_workspace(rows, lay.max_blocks, topk, G, DEV)
 
     def step():
+        if fused == "step":
+            gpu.m3s_decode_step(cache, k_new, v_new, i_new, s_new_rows, cu_q, seq_t, R, row_req, row_len, req_blk,
+                                q_idx, q, bt, lay.max_blocks, topk, 0.3, 0, ids, out, ws_f, status)
+            return
         if prefill:
             gpu.m3s_store(cache, k_new, v_new, i_new, s_new, status)
             gpu.m3s_prefill_rows(cu_q, seq_t, R, rows.num_groups, status, out=rows)
