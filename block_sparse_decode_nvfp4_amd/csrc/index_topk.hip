@@ -613,19 +613,16 @@ __global__ __launch_bounds__(WAVES * 64) void index_scan_kernel(IndexArgs a) {
   scan_body<FMT, NT, WAVES, H, false>(a, blockIdx.x, gridDim.x);
 }
 
-constexpr int kTailReqs = 8;  // requests per tail workgroup (at most)
-
-// Tail workgroup t of the decode step kernel: requests [b0, b1), at most kTailReqs (the
-// launcher's split). It stores the step's new rows (every token in its share
-// [t T / ntail, (t + 1) T / ntail) of the T tokens, and again the tokens of its own
-// requests, so that those are in the planes before it reads them: writing the same
-// bytes twice is harmless), waits for its stores, then scores each of its requests'
-// blocks that hold a new token against the request's rows with the scan's
-// arithmetic, one block per wave (a request's q_len <= 16 new tokens touch at most
-// two blocks, so at most 16 units for the 16 waves). No other workgroup reads those
-// pages in this launch. Every load that does not need the stores (the rows to
-// store, the slots, the block-table entries, the queries) is issued before the
-// first wait.
+// Tail workgroup t of the decode step kernel: requests [b0, b1) (the launcher's split).
+// It stores the step's new rows (every token in its share [t T / ntail, (t + 1) T / ntail)
+// of the T tokens, and again the tokens of its own requests, so that those are in the
+// planes before it reads them: writing the same bytes twice is harmless), waits for its
+// stores, then scores each of its requests' blocks that hold a new token against the
+// request's rows with the scan's arithmetic, one block per wave at a time (a request's
+// q_len <= 16 new tokens touch at most two blocks). No other workgroup reads those pages
+// in this launch. For the wave's first block and the first 64 requests' slot checks,
+// every load that does not need the stores (the rows to store, the slots, the
+// block-table entries, the query) is issued before the first wait.
 template <int FMT>
 __device__ __forceinline__ void tail_body(const IndexArgs& a, const StoreArgs& s, int t, int ntail) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -633,7 +630,7 @@ __device__ __forceinline__ void tail_body(const IndexArgs& a, const StoreArgs& s
   const int B = a.num_reqs;
   const int b0 = (int)((int64_t)t * B / ntail), b1 = (int)((int64_t)(t + 1) * B / ntail);
   // the own requests' tokens lie in [lo, hi) (all rows of an accepted request are in
-  // [0, num_rows), and num_tokens = num_rows); the wave's tail unit (ub, uj)
+  // [0, num_rows), and num_tokens = num_rows); the wave's first tail unit (ub, uj)
   int lo = 0x7FFFFFFF, hi = 0, nu = 0, ub = -1, uj = 0;
   for (int b = b0; b < b1; ++b) {
     const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
@@ -658,21 +655,22 @@ __device__ __forceinline__ void tail_body(const IndexArgs& a, const StoreArgs& s
     store_issue(s, r1 < sh1 ? r1 : -1, l16, sh[p]);
     store_issue(s, r2 < ow1 ? r2 : -1, l16, ow[p]);
   }
-  // decode convention, lanes (k, i) of the first waves: token i of request b0 + k goes
-  // to position seq_len - q_len + i of that request's block table
-  int chk_slot = -1, chk_want = -1;
-  if (tid < 16 * kTailReqs && b0 + (tid >> 4) < b1) {
-    const int b = b0 + (tid >> 4), i = tid & 15;
+  // decode convention, lanes (k, i): token i of request b goes to position
+  // seq_len - q_len + i of that request's block table (64 requests per pass)
+  auto check = [&](int b, int& slot, int& want) {
+    const int i = tid & 15;
     const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
     const int ql = q1 - q0;
     if (step_request_ok(q0, q1, sl, a.num_rows) && i < ql && q0 + i < T) {
       const int pos = sl - ql + i, j = pos / kPage;
       const int pg = j < a.max_blocks ? a.block_table[(int64_t)b * a.bt_stride + j] : -1;
-      chk_slot = s.slots[q0 + i];
-      if (pg >= 0 && pg < a.num_pages) chk_want = pg * kPage + pos % kPage;
+      slot = s.slots[q0 + i];
+      if (pg >= 0 && pg < a.num_pages) want = pg * kPage + pos % kPage;
     }
-  }
-  // the wave's unit: its page entry and its query tile
+  };
+  int chk_slot = -1, chk_want = -1;
+  if (b0 + (tid >> 4) < b1) check(b0 + (tid >> 4), chk_slot, chk_want);
+  // the wave's first unit: its page entry and its query tile
   int pg = -1;
   QueryTile qt;
   if (ub >= 0 && uj < a.max_blocks) {
@@ -684,29 +682,55 @@ __device__ __forceinline__ void tail_body(const IndexArgs& a, const StoreArgs& s
     store_commit<FMT>(s, l16, sh[p]);
     store_commit<FMT>(s, l16, ow[p]);
   }
-  // rows past the first 192 of either range (not met by a well-formed step)
+  // rows past the first 192 of either range (more than 64 tokens per tail workgroup)
   for (int64_t rr = sh0 + 192 + (tid >> 4); rr < sh1; rr += 64) store_row<FMT>(s, rr, l16);
   for (int64_t rr = ow0 + 192 + (tid >> 4); rr < ow1; rr += 64) store_row<FMT>(s, rr, l16);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have landed (vmcnt counts stores)
   __syncthreads();                // ... and every wave's, before any page read
   if (chk_want >= 0 && chk_slot != chk_want) set_status(a.status, kDevStepSlot);
-  if (ub < 0) return;
-  if (uj >= a.max_blocks) {
-    if (lane == 0) set_status(a.status, kDevBadLength);
-    return;
+  for (int b = b0 + 64 + (tid >> 4); b < b1; b += 64) {  // further requests' slot checks
+    int sl2 = -1, want2 = -1;
+    check(b, sl2, want2);
+    if (want2 >= 0 && sl2 != want2) set_status(a.status, kDevStepSlot);
   }
-  if (pg < 0 || pg >= a.num_pages) {
-    if (lane == 0) set_status(a.status, kDevBadPage);
-    if (G == 0 && n < qt.ql) {
-      const int64_t o = (int64_t)(qt.r0 + n) * a.max_blocks + uj;
-      a.ws_score[o] = -INFINITY;
-      a.ws_bound[o] = 0.f;
+  // the wave's units: u = w, w + 16, ... of the workgroup's tail blocks in request order
+  auto score_unit = [&](int b, int j, int pgv, QueryTile& q) {
+    if (j >= a.max_blocks) {
+      if (lane == 0) set_status(a.status, kDevBadLength);
+      return;
     }
-    return;
+    if (pgv < 0 || pgv >= a.num_pages) {
+      if (lane == 0) set_status(a.status, kDevBadPage);
+      if (G == 0 && n < q.ql) {
+        const int64_t o = (int64_t)(q.r0 + n) * a.max_blocks + j;
+        a.ws_score[o] = -INFINITY;
+        a.ws_bound[o] = 0.f;
+      }
+      return;
+    }
+    PageBuf pa;
+    load_page<FMT>(pa, a, pgv, n, G);
+    score_page<FMT>(pa, q, a, j, n, G);
+  };
+  if (ub < 0) return;
+  score_unit(ub, uj, pg, qt);
+  if (nu <= 16) return;
+  int u = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
+    if (!step_request_ok(q0, q1, sl, a.num_rows)) continue;
+    const int j_lo = (sl - (q1 - q0)) / kPage, j_hi = (sl + kPage - 1) / kPage;
+    for (int j = j_lo; j < j_hi; ++j, ++u) {
+      if (u < 16 || u % 16 != w) continue;
+      QueryTile q2;
+      int pg2 = -1;
+      if (j < a.max_blocks) {
+        pg2 = a.block_table[(int64_t)b * a.bt_stride + j];
+        load_query<FMT>(q2, a, b, 0, n, G);
+      }
+      score_unit(b, j, pg2, q2);
+    }
   }
-  PageBuf pa;
-  load_page<FMT>(pa, a, pg, n, G);
-  score_page<FMT>(pa, qt, a, uj, n, G);
 }
 
 // The decode step's first kernel: workgroup 0 builds the row map (m3s_decode_rows),
@@ -1365,13 +1389,16 @@ hipError_t launch_index_topk_attend(const IndexArgs& ia, const AttendArgs& aa, h
 
 hipError_t launch_decode_step(const IndexArgs& ia, const AttendArgs& aa, const StoreArgs& s, const RowsArgs& r,
                               hipStream_t stream) {
-  // tail workgroups: at most kTailReqs requests each (tail_body relies on it), four
-  // while the batch is small (measured at 8 requests of 150K: one tail workgroup of
-  // eight outlasts the scan, the step went from 46.3 to 50.8 us); the scan keeps the
-  // other CUs, fewer when there are fewer than 16 blocks per workgroup
+  // tail workgroups: four requests each up to 32 requests (measured at 8 requests of
+  // 150K: one tail workgroup of eight outlasts the scan, the step went from 46.3 to
+  // 50.8 us), eight beyond, at most an eighth of the CUs (more requests per tail
+  // workgroup beyond that); the scan keeps the other CUs, fewer when there are fewer
+  // than 16 blocks per workgroup
   const int B = ia.num_reqs;
-  const int per = B <= 32 ? 4 : kTailReqs;
-  const int ntail = B > 0 ? (B + per - 1) / per : (s.num_tokens > 0 ? 1 : 0);
+  const int per = B <= 32 ? 4 : 8;
+  const int max_tail = ia.scan_grid / 8 > 1 ? ia.scan_grid / 8 : 1;
+  int ntail = B > 0 ? (B + per - 1) / per : (s.num_tokens > 0 ? 1 : 0);
+  if (ntail > max_tail) ntail = max_tail;
   int64_t nscan = (int64_t)ia.scan_grid - 1 - ntail;
   const int64_t units_upper = (int64_t)B * ia.max_blocks;
   if (nscan * 16 > units_upper) nscan = (units_upper + 15) / 16;

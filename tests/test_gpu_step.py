@@ -154,6 +154,16 @@ def test_step_many_requests(gpu):
     assert sa == sb == 0
 
 
+def test_step_max_requests(gpu):
+    """4096 requests (the most a call takes) of one row each: 512 tail workgroups, more
+    than the CUs, beside a single scan workgroup."""
+    rng = np.random.default_rng(13)
+    seq = [int(x) for x in rng.integers(1, 1500, size=4096)]
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=1, G=2)
+    sa, sb = _run_both(gpu, wc, "nvfp4", 4, 1.0)
+    assert sa == sb == 0
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 def test_step_pad_rows_and_rejected_request(gpu, fmt):
     wc = W.make_case(CFG0, DEV, seq_lens=[9000, 300, 40_000, 129], q_len=[8, 4, 16, 2], G=4)
