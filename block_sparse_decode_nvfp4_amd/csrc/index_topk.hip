@@ -113,15 +113,7 @@ struct QueryTile {
 // qe0 = sum of |r|: the scorer's error bound is 6 smax (2^-15 qs0 + qe0) per
 // block, the 2^-15 covering any order of the <= 383 fp32 additions of the three
 // chained MFMAs (383 * 2^-24 < 2^-15).
-__device__ __forceinline__ void build_query_mx(QueryTile& q, const IndexArgs& a, int row, int n, int G) {
-  u32x4 raw[4] = {};
-  if (row >= 0) {
-    const uint16_t* qp = a.q_idx + (int64_t)row * a.q_stride;
-    raw[0] = *reinterpret_cast<const u32x4*>(qp + 16 * G);
-    raw[1] = *reinterpret_cast<const u32x4*>(qp + 16 * G + 8);
-    raw[2] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G);
-    raw[3] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G + 8);
-  }
+__device__ __forceinline__ void query_from_raw_mx(QueryTile& q, const u32x4 (&raw)[4], int n, int G) {
   // half 0 (raw[0..1]) lies in block G / 2, half 1 (raw[2..3]) in block 2 + G / 2;
   // lanes G and G ^ 1 hold the two halves of each block
   uint32_t mh[2] = {0u, 0u};
@@ -198,19 +190,48 @@ __device__ __forceinline__ void build_query_mx(QueryTile& q, const IndexArgs& a,
   q.unscale = 1.0f;
 }
 
-// The B operand of query row `row` (or zeros when row < 0) in lane (n, G), with
-// the sums the error bound needs. Lanes n of one 16-lane column share a row.
+// Lane (n, G)'s share of query row `row` (zeros when row < 0), as the B operand
+// takes it: NVFP4 dims [32 G, 32 G + 32); MXFP4 dims [16 G, 16 G + 16) and
+// [64 + 16 G, 64 + 16 G + 16).
 template <int FMT>
-__device__ __forceinline__ void build_query(QueryTile& q, const IndexArgs& a, int row, int n, int G) {
-  if (FMT == 2) {
-    build_query_mx(q, a, row, n, G);
-    return;
-  }
-  u32x4 raw[4] = {};
-  if (row >= 0) {
-    const uint16_t* qp = a.q_idx + (int64_t)row * a.q_stride + 32 * G;
+__device__ __forceinline__ void query_raw(u32x4 (&raw)[4], const IndexArgs& a, int row, int G) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 8 * s);
+  for (int s = 0; s < 4; ++s) raw[s] = u32x4{0u, 0u, 0u, 0u};
+  if (row >= 0) {
+    const uint16_t* qp = a.q_idx + (int64_t)row * a.q_stride;
+    if (FMT == 1) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qp + 32 * G + 8 * s);
+    } else {
+      raw[0] = *reinterpret_cast<const u32x4*>(qp + 16 * G);
+      raw[1] = *reinterpret_cast<const u32x4*>(qp + 16 * G + 8);
+      raw[2] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G);
+      raw[3] = *reinterpret_cast<const u32x4*>(qp + 64 + 16 * G + 8);
+    }
+  }
+}
+
+// query_raw from a copy of the row in LDS (qs: the row's 128 bf16 values).
+template <int FMT>
+__device__ __forceinline__ void query_raw_lds(u32x4 (&raw)[4], const uint16_t* qs, int G) {
+  if (FMT == 1) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) raw[s] = *reinterpret_cast<const u32x4*>(qs + 32 * G + 8 * s);
+  } else {
+    raw[0] = *reinterpret_cast<const u32x4*>(qs + 16 * G);
+    raw[1] = *reinterpret_cast<const u32x4*>(qs + 16 * G + 8);
+    raw[2] = *reinterpret_cast<const u32x4*>(qs + 64 + 16 * G);
+    raw[3] = *reinterpret_cast<const u32x4*>(qs + 64 + 16 * G + 8);
+  }
+}
+
+// The B operand built from the lane's share of its row (query_raw), with the sums
+// the error bound needs. Lanes n of one 16-lane column share a row.
+template <int FMT>
+__device__ __forceinline__ void query_from_raw(QueryTile& q, const u32x4 (&raw)[4], int n, int G) {
+  if (FMT == 2) {
+    query_from_raw_mx(q, raw, n, G);
+    return;
   }
   uint32_t mx = 0;
 #pragma unroll
@@ -237,23 +258,39 @@ __device__ __forceinline__ void build_query(QueryTile& q, const IndexArgs& a, in
   }
 }
 
-// Query tile k of work group b: the group's rows 16 k .. 16 k + 15 (fewer at its end).
+// The B operand of query row `row` (or zeros when row < 0) in lane (n, G).
 template <int FMT>
-__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int k, int n, int G) {
-  const int g0 = a.cu_q[b];
+__device__ __forceinline__ void build_query(QueryTile& q, const IndexArgs& a, int row, int n, int G) {
+  u32x4 raw[4];
+  query_raw<FMT>(raw, a, row, G);
+  query_from_raw<FMT>(q, raw, n, G);
+}
+
+// The rows of query tile k of work group b, given g0 = cu_q[b] and g1 = cu_q[b + 1]:
+// rows g0 + 16 k .. (at most 16, fewer at the group's end), and their causal lengths,
+// from the row map, or in closed form for the decode step (its row map is written
+// by the same launch): row r of request b sees step_base + r tokens, step_base =
+// seq_len - q_len + 1 - cu_q[b].
+__device__ __forceinline__ void query_rows(QueryTile& q, const IndexArgs& a, int b, int k, int g0, int g1,
+                                           bool closed, int step_base, int n) {
   q.b = b;
   q.r0 = g0 + 16 * k;
-  q.ql = min(max(a.cu_q[b + 1] - q.r0, 0), 16);
-  if (a.seq_lens) {
-    // decode step: row r of request b sees seq_len - q_len + 1 + (r - cu_q[b]) tokens
-    // (the row map is written by the same launch, so it is derived here)
-    const int base = a.seq_lens[b] - (a.cu_q[b + 1] - g0) + 1 - g0;
-    q.min_len = q.ql > 0 ? base + q.r0 : 0x7FFFFFFF;
-    q.len_n = n < q.ql ? base + q.r0 + n : 0;
+  q.ql = min(max(g1 - q.r0, 0), 16);
+  if (closed) {
+    q.min_len = q.ql > 0 ? step_base + q.r0 : 0x7FFFFFFF;
+    q.len_n = n < q.ql ? step_base + q.r0 + n : 0;
   } else {
     q.min_len = q.ql > 0 ? a.row_len[q.r0] : 0x7FFFFFFF;
     q.len_n = n < q.ql ? a.row_len[q.r0 + n] : 0;
   }
+}
+
+// Query tile k of work group b: the group's rows 16 k .. 16 k + 15 (fewer at its end).
+template <int FMT>
+__device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int b, int k, int n, int G) {
+  const int g0 = a.cu_q[b], g1 = a.cu_q[b + 1];
+  const bool closed = a.seq_lens != nullptr;
+  query_rows(q, a, b, k, g0, g1, closed, closed ? a.seq_lens[b] - (g1 - g0) + 1 - g0 : 0, n);
   build_query<FMT>(q, a, n < q.ql ? q.r0 + n : -1, n, G);
 }
 
@@ -471,16 +508,21 @@ __device__ __forceinline__ bool step_request_ok(int q0, int q1, int sl, int num_
 // Wave 0: s_blk[b] = exclusive prefix over the requests of each accepted request's
 // blocks with no new token, floor((seq_len - q_len) / 128) (0 for the others). The
 // decode step's scan takes these blocks; the tail workgroups the rest.
-__device__ __forceinline__ void step_prefix_old(const IndexArgs& a, int* s_blk) {
+// s_cq[b] = cu_q[b] (b <= B) and s_sb[b] = seq_len - q_len + 1 - cu_q[b], the rows'
+// closed-form length base (query_rows), for the scan's query loads.
+__device__ __forceinline__ void step_prefix_old(const IndexArgs& a, int* s_blk, int* s_cq, int* s_sb) {
   const int lane = threadIdx.x & 63;
   const int B = a.num_reqs;
   int carry = 0;
+  if (lane == 0) s_cq[0] = a.cu_q[0];
   for (int base = 0; base < B; base += 64) {
     const int b = base + lane;
     int nb = 0;
     if (b < B) {
       const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1], sl = a.seq_lens[b];
       if (step_request_ok(q0, q1, sl, a.num_rows)) nb = (sl - (q1 - q0)) / kPage;
+      s_cq[b + 1] = q1;
+      s_sb[b] = sl - (q1 - q0) + 1 - q0;
     }
     const int x = wave_incl_sum(nb);
     if (b < B) s_blk[b] = carry + x - nb;
@@ -499,12 +541,26 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
   __shared__ int s_unit[kScanChunk];  // request * kMaxBlocks + block; -1: not scored
   __shared__ int s_page[kScanChunk];  // page; -1: unusable
   __shared__ int s_ctr;
+  // decode step: cu_q and the rows' length base, read by the prefix anyway; a wave
+  // that meets a new request issues its query loads from these, with no dependent
+  // global load first (under the scan's load that round trip takes microseconds).
+  // Elsewhere a wave reads cu_q itself: loading it in the prologue measured slower.
+  __shared__ int s_cq[STEP ? M3S_MAX_REQS_INTERNAL + 1 : 1];
+  __shared__ int s_sb[STEP ? M3S_MAX_REQS_INTERNAL : 1];
+  // decode step: the index query rows of the slice's requests (when they fit), loaded
+  // once by the workgroup beside the block-table entries, instead of by every wave
+  // that meets a request (about a tenth of the workgroup's vector load instructions
+  // otherwise, issued while its waves queue to issue their page loads; measured, the
+  // MXFP4 step 3 us faster, NVFP4 0.3 us); rows padded against bank conflicts
+  constexpr int kStageRows = 64, kStageRow = 136;
+  __shared__ __attribute__((aligned(16))) uint16_t s_qst[STEP ? kStageRows : 1][kStageRow];
+  static_assert(NT > 1 || H == 1, "one query tile per group: one pass");
   const int tid = threadIdx.x, lane = tid & 63;
   const int n = lane & 15, G = lane >> 4;
   const int B = a.num_reqs;
   if constexpr (STEP) {
     static_assert(NT == 1 && H == 1, "the decode step's scan");
-    if (tid < 64) step_prefix_old(a, s_blk);
+    if (tid < 64) step_prefix_old(a, s_blk, s_cq, s_sb);
   } else {
     for (int i = tid; i <= B; i += kScanWaves * 64) s_blk[i] = a.req_blk[i];
   }
@@ -527,8 +583,23 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
     return __builtin_amdgcn_readlane(v, 0);
   };
 
-  for (int64_t c0 = w0; c0 < w1; c0 += kScanChunk) {  // uniform over the workgroup
-    const int cnt = (int)min((int64_t)kScanChunk, w1 - c0);
+  // decode step: rows [q_lo, q_lo + q_n) are staged in s_qst, 16 B per thread, loaded
+  // here and written to LDS after the block-table loads are issued (one round trip)
+  int q_lo = 0, q_n = 0;
+  u32x4 q_chunk = {0u, 0u, 0u, 0u};
+  if constexpr (STEP) {
+    static_assert(kStageRows * 16 <= kScanWaves * 64, "one staged chunk per thread");
+    if (w1 > w0) {
+      q_lo = s_cq[req_of(w0)];
+      q_n = s_cq[req_of(w1 - 1) + 1] - q_lo;
+      if (q_n <= 0 || q_n > kStageRows || q_lo < 0 || q_lo + q_n > a.num_rows) q_n = 0;
+    }
+    if (tid < q_n * 16)
+      q_chunk = *reinterpret_cast<const u32x4*>(a.q_idx + (int64_t)(q_lo + (tid >> 4)) * a.q_stride + 8 * (tid & 15));
+  }
+
+  // the LDS unit table of chunk [c0, c0 + cnt): each unit's key and page
+  auto build_table = [&](int64_t c0, int cnt) {
     for (int i = tid; i < cnt; i += kScanWaves * 64) {
       const int64_t u = (c0 + i) / H;  // the H passes of a block are adjacent units
       const int half = (int)((c0 + i) - u * H);
@@ -551,17 +622,43 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
       s_unit[i] = key;
       s_page[i] = pg;
     }
+  };
+  // the first chunk's table is built before the loop, so the staged query chunk is
+  // written (and dead) before the claim loop
+  if (w1 > w0) build_table(w0, (int)min((int64_t)kScanChunk, w1 - w0));
+  if constexpr (STEP) {
+    if (tid < q_n * 16) *reinterpret_cast<u32x4*>(&s_qst[tid >> 4][8 * (tid & 15)]) = q_chunk;
+  }
+
+  for (int64_t c0 = w0; c0 < w1; c0 += kScanChunk) {  // uniform over the workgroup
+    const int cnt = (int)min((int64_t)kScanChunk, w1 - c0);
+    if (c0 != w0) build_table(c0, cnt);
     if (tid == 0) s_ctr = 0;
     __syncthreads();
     QueryTile qt[NT];
     int qb = -1;  // (work group, pass) whose query tiles qt holds
+    // query tile k of (group, pass) bh
+    auto load_tile = [&](int k, int bh) {
+      const int b = bh / H;
+      if constexpr (STEP) {
+        query_rows(qt[k], a, b, k, s_cq[b], s_cq[b + 1], true, s_sb[b], n);
+        const int row = n < qt[k].ql ? qt[k].r0 + n : -1;
+        u32x4 raw[4];
+        if (row >= q_lo && row < q_lo + q_n) query_raw_lds<FMT>(raw, s_qst[row - q_lo], G);
+        else query_raw<FMT>(raw, a, row, G);
+        query_from_raw<FMT>(qt[k], raw, n, G);
+      } else {
+        query_rows(qt[k], a, b, NT * (bh % H) + k, a.cu_q[b], a.cu_q[b + 1], false, 0, n);
+        build_query<FMT>(qt[k], a, n < qt[k].ql ? qt[k].r0 + n : -1, n, G);
+      }
+    };
     auto process = [&](const PageBuf& buf, int key, int pg) {
       if (key < 0) return;
       const int bh = key / kMaxBlocks, j = key - bh * kMaxBlocks;
-      if (bh != qb) {
+      if (bh != qb) {  // NT = 1: the query loads go out right behind the page's
         qb = bh;
 #pragma unroll
-        for (int k = 0; k < NT; ++k) load_query<FMT>(qt[k], a, bh / H, NT * (bh % H) + k, n, G);
+        for (int k = 0; k < NT; ++k) load_tile(k, bh);
       }
       if (pg >= 0) {
         if constexpr (NT == 1) score_page<FMT>(buf, qt[0], a, j, n, G);
@@ -595,7 +692,7 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
           qb = bh;
 #pragma unroll
           for (int k = 0; k < NT; ++k) {
-            load_query<FMT>(qt[k], a, bh / H, NT * (bh % H) + k, n, G);
+            load_tile(k, bh);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
