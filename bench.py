@@ -414,6 +414,41 @@ def ceilings(m3s, cfg, dev, layers):
             res[key] = {"us_per_launch": round(best * 1e3, 2),
                         "gbs": round(npages * 128 * 72 / (best * 1e-3) / 1e9, 1)}
             log(f"[ceilings] {key}: {best * 1e3:.2f} us, {res[key]['gbs']:.0f} GB/s")
+
+    # plain streams for comparison (probe mode 2): the same bytes front to back, and a
+    # stream of every layer's bytes at once (past the Infinity Cache, no launch cycling)
+    def stream(pl, n, grid, reps_, cycle):
+        sk = torch.zeros(grid, dtype=torch.int32, device=dev)
+        idx = torch.arange(n, dtype=torch.int32, device=dev)
+        for L in range(len(pl)):
+            m3s.m3s_probe_page_reads(pl[L][0], pl[L][1], idx, 2, sk)
+        best = None
+        for trial in range(3):
+            ea = torch.cuda.Event(enable_timing=True)
+            eb = torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(3_000_000)
+            ea.record()
+            for i in range(reps_):
+                L = i % len(pl) if cycle else 0
+                m3s.m3s_probe_page_reads(pl[L][0], pl[L][1], idx, 2, sk, check=False)
+            eb.record()
+            torch.cuda.synchronize()
+            t = ea.elapsed_time(eb) / reps_
+            best = t if best is None else min(best, t)
+        return best
+
+    for grid in (cus, 2 * cus):
+        best = stream(planes, npages, grid, reps, True)
+        key = f"stream_same_bytes_grid{grid}"
+        res[key] = {"us_per_launch": round(best * 1e3, 2), "gbs": round(npages * 128 * 72 / (best * 1e-3) / 1e9, 1)}
+        log(f"[ceilings] {key}: {best * 1e3:.2f} us, {res[key]['gbs']:.0f} GB/s")
+    big = [(torch.cat([p[0] for p in planes]), torch.cat([p[1] for p in planes]))]
+    nb_ = big[0][0].shape[0]
+    del planes
+    best = stream(big, nb_, 8 * cus, 10, False)
+    key = f"stream_{nb_ * 128 * 72 >> 20}MB_grid{8 * cus}"
+    res[key] = {"us_per_launch": round(best * 1e3, 2), "gbs": round(nb_ * 128 * 72 / (best * 1e-3) / 1e9, 1)}
+    log(f"[ceilings] {key}: {best * 1e3:.2f} us, {res[key]['gbs']:.0f} GB/s")
     print(json.dumps(res), flush=True)
 
 

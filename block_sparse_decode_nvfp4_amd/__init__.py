@@ -431,7 +431,7 @@ def m3s_probe_page_reads(payload, scales, pages, mode: int, sink, stream=None, c
     """Measurement only: read the listed pages with the index scan's load pattern
     (see include/m3s.h). Every page id must lie inside the planes: with check=True the
     ids are checked here (a device-to-host read); a timing loop checks once, then passes
-    check=False."""
+    check=False. Mode 2 streams the first pages.numel() pages of both planes instead."""
     torch = _torch()
     _need(payload, "payload", torch.uint8)
     _need(scales, "scales", torch.uint8)
@@ -443,6 +443,8 @@ def m3s_probe_page_reads(payload, scales, pages, mode: int, sink, stream=None, c
     # host-side bounds check of every page id (the kernel trusts them)
     if check and pages.numel() and (int(pages.min()) < 0 or int(pages.max()) >= P):
         raise ValueError("page id outside the planes")
+    if mode == 2 and pages.numel() > P:
+        raise ValueError("the stream reads more pages than the planes hold")
     st = load().m3s_probe_page_reads(_ptr(payload), _ptr(scales), _ptr(pages), pages.numel(), mode, _ptr(sink),
                                      sink.numel(), _stream(stream))
     _check("m3s_probe_page_reads", st)

@@ -10,6 +10,9 @@
 //   mode 0: 2 B per lane per 16-token tile (token 16 i + n, bytes 2G..2G+1), as the
 //           NVFP4 scan loads them;
 //   mode 1: one 16 B load per lane covering the whole 1 KB scale block of the page.
+// Mode 2 is a plain stream for comparison: the first num_units pages of both planes
+// (the same bytes as num_units pages) read front to back with 16-byte loads, every
+// thread striding over the grid; the page list is not read.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,14 +69,45 @@ __global__ __launch_bounds__(1024) void probe_kernel(const uint8_t* pay, const u
   }
 }
 
+__global__ __launch_bounds__(1024) void stream_kernel(const u32x4* pay, const u32x4* scl, int64_t n_pay,
+                                                       int64_t n_scl, uint32_t* sink) {
+  __shared__ uint32_t s_acc[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + tid; i < n_pay; i += stride) {
+    const u32x4 v = pay[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + tid; i < n_scl; i += stride) {
+    const u32x4 v = scl[i];
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= __shfl_xor(acc, m, 64);
+  if (lane == 0) s_acc[w] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < 16; ++i) t ^= s_acc[i];
+    sink[blockIdx.x] = t;
+  }
+}
+
 }  // namespace
 
 extern "C" m3s_status m3s_probe_page_reads(const uint8_t* payload, const uint8_t* scales, const int32_t* pages,
                                            int32_t num_units, int32_t mode, uint32_t* sink, int32_t num_sink,
                                            hipStream_t stream) {
-  if (!payload || !scales || !pages || !sink || num_units < 0 || (mode != 0 && mode != 1) || num_sink < 1)
+  if (!payload || !scales || !pages || !sink || num_units < 0 || mode < 0 || mode > 2 || num_sink < 1)
     return M3S_ERR_INVALID_ARG;
   if (num_units == 0) return M3S_OK;
+  if (mode == 2) {
+    hipLaunchKernelGGL(stream_kernel, dim3((unsigned)num_sink), dim3(1024), 0, stream,
+                       reinterpret_cast<const u32x4*>(payload), reinterpret_cast<const u32x4*>(scales),
+                       (int64_t)num_units * (128 * 64 / 16), (int64_t)num_units * (128 * 8 / 16), sink);
+    return hipGetLastError() == hipSuccess ? M3S_OK : M3S_ERR_HIP;
+  }
   hipLaunchKernelGGL(probe_kernel, dim3((unsigned)num_sink), dim3(1024), 0, stream, payload, scales, pages,
                      num_units, mode, sink);
   return hipGetLastError() == hipSuccess ? M3S_OK : M3S_ERR_HIP;

@@ -454,7 +454,10 @@ int32_t m3s_version(void);
  * time gives the memory system's ceiling for that pattern. One 16-wave workgroup per
  * sink entry (pass the CU count); each writes one folded word to sink[num_sink].
  * mode 0: 2-byte scale loads per 16-token tile, as the NVFP4 scan loads them;
- * mode 1: one 16-byte load per lane over the page's 1 KB scale block.
+ * mode 1: one 16-byte load per lane over the page's 1 KB scale block;
+ * mode 2: a plain stream of the same number of bytes for comparison: the first
+ *   num_units pages of both planes front to back, 16-byte loads striding over the
+ *   grid (pages is not read; num_units must not exceed the planes' pages).
  * Returns M3S_ERR_INVALID_ARG for null pointers, num_units < 0, num_sink < 1 or
  * another mode. Page ids are not checked: every pages[u] must lie in the planes.
  */

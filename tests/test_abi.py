@@ -264,7 +264,8 @@ def test_probe_rejects_bad_arguments(lib):
     one = ctypes.c_void_p(16)
     assert f(None, one, one, 1, 0, one, 1, None) == m3s.ERR_INVALID_ARG
     assert f(one, one, one, -1, 0, one, 1, None) == m3s.ERR_INVALID_ARG
-    assert f(one, one, one, 1, 2, one, 1, None) == m3s.ERR_INVALID_ARG
+    assert f(one, one, one, 1, 3, one, 1, None) == m3s.ERR_INVALID_ARG
+    assert f(one, one, one, 1, -1, one, 1, None) == m3s.ERR_INVALID_ARG
     assert f(one, one, one, 1, 0, one, 0, None) == m3s.ERR_INVALID_ARG
     assert f(one, one, one, 0, 0, one, 1, None) == m3s.OK
 
