@@ -5,7 +5,8 @@ checked against the oracle elsewhere; here the one-launch step must change nothi
 
 Cases cover the decode workloads' shapes (8 x 8 rows at 150K, 48 lognormal requests),
 tails that cross a page boundary, steps whose rows are the whole context, single-block
-requests, many requests (many tail workgroups), pad rows, a rejected request, a bad page
+requests, many requests (many tail workgroups), slices spanning many requests (query rows staged
+in LDS or not), pad rows, a rejected request, a bad page
 in a tail block, and a slot mapping that breaks the decode convention inside one page
 (flagged, results still equal since the page has one writer). The new tokens' slots start
 out holding random bytes, so a read of a page before the step's store has landed shows."""
@@ -161,6 +162,19 @@ def test_step_max_requests(gpu):
     seq = [int(x) for x in rng.integers(1, 1500, size=4096)]
     wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=1, G=2)
     sa, sb = _run_both(gpu, wc, "nvfp4", 4, 1.0)
+    assert sa == sb == 0
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_step_wide_slices(gpu, fmt):
+    """1024 requests of 16 rows with 1 to 5 blocks before their new tokens: a scan
+    workgroup's slice spans several requests, so some slices' rows fit the 64 rows a
+    workgroup stages in LDS and others exceed them (their waves then read the query rows
+    from HBM)."""
+    rng = np.random.default_rng(17)
+    seq = [int(x) for x in rng.integers(150, 700, size=1024)]
+    wc = W.make_case(CFG0, DEV, seq_lens=seq, q_len=16, G=2)
+    sa, sb = _run_both(gpu, wc, fmt, 4, 1.0)
     assert sa == sb == 0
 
 
