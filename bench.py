@@ -459,7 +459,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--config", default="b8x8_150k")
     ap.add_argument("--layers", type=int, default=8)
-    ap.add_argument("--cpu-requests", type=int, default=2)
+    ap.add_argument("--cpu-requests", type=int, default=6)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--calls", choices=("step", "two", "separate"), default="step",
