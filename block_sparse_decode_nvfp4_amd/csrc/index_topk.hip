@@ -676,8 +676,15 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
     };
     // one page in flight per wave; the other waves of the SIMD cover its latency
     // (measured: for the prefill variant a second page in flight per wave was
-    // slower, its time goes to the scoring itself)
-    while (true) {
+    // slower, its time goes to the scoring itself). In the NVFP4 decode step only 12 of
+    // the 16 waves claim pages: with every wave in, the CU's vector-memory path is full
+    // from the first round and the youngest waves' first pages come back last. Measured
+    // (same-box A/B, steps per graph replay): 12 fastest of 8 to 16 at 8 x 8 rows at 150K
+    // (44.8 against 46.3 us), the skewed batch (52.4 against 54.2) and 48 lognormal
+    // requests (181.3 against 185.6). The MXFP4 step (more arithmetic per page) and the
+    // separate scan measured no faster or slower with 12 and keep all 16.
+    constexpr int kClaimWaves = STEP && FMT == 1 ? 12 : kScanWaves;
+    while ((tid >> 6) < kClaimWaves) {
       const int c = claim();
       if (c >= cnt) break;
       // uniform over the wave (read from LDS at a uniform index): in scalar registers,
