@@ -533,7 +533,8 @@ __device__ __forceinline__ void step_prefix_old(const IndexArgs& a, int* s_blk, 
 
 // STEP: the decode step's scan (NT = H = 1): its units are each accepted request's
 // blocks with no new token (step_prefix_old), and the rows' causal lengths come from
-// seq_lens (load_query), since the row map is written by the same launch.
+// seq_lens (query_rows in closed form), since the row map is written by the same
+// launch.
 template <int FMT, int NT, int WAVES, int H, bool STEP>
 __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
   constexpr int kScanWaves = WAVES;
