@@ -294,6 +294,21 @@ __device__ __forceinline__ void load_query(QueryTile& q, const IndexArgs& a, int
   build_query<FMT>(q, a, n < q.ql ? q.r0 + n : -1, n, G);
 }
 
+// NVFP4 K tile i of a page as the MFMA A operand (kd[c]: k-step c) and its two scales.
+// The tile's words are pinned where the decode starts, so that a caller's order of
+// decodes is kept (each decoded tile holds 16 registers).
+__device__ __forceinline__ void decode_tile_nv(const PageBuf& p, int i, f16x8 (&kd)[4], f16x2& sc) {
+  u32x4 kw = p.kr[i];
+  uint32_t ksw = p.ks[i];
+  asm volatile("" : "+v"(kw), "+v"(ksw));
+  const auto sf = __builtin_amdgcn_cvt_pk_f32_fp8((int)ksw, false);
+  sc = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[1]));
+  const f16x8 s0 = {sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0], sc[0]};
+  const f16x8 s1 = {sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1], sc[1]};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) kd[c] = fp4x8_to_f16_unscaled(kw[c]) * (c < 2 ? s0 : s1);
+}
+
 // S^T tile i of a page against NT query tiles: acc[k][v] = (scaled) score of
 // token 16 i + 4 G + v against the query in column n (lane (n, G)) of tile k.
 // The K tile is decoded once for all NT tiles, and each column's result is the
@@ -412,11 +427,26 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
   }
   f16x2 smx = {(_Float16)0.f, (_Float16)0.f};  // largest scale of groups (2G, 2G+1) seen by this lane
   float smx_mx = 0.f;                          // MXFP4: largest E8M0 scale of group G
+  // NVFP4: tile i + 1 is decoded (VALU) while tile i's NT x 4 MFMAs run, one tile ahead
+  f16x8 kd[4], kn[4];
+  f16x2 sc_cur, sc_next;
+  if constexpr (FMT == 1) decode_tile_nv(p, 0, kd, sc_cur);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     f16x2 sc;
     f32x4 acc[NT];
-    tile_scores_n<FMT, NT>(p, q, i, sc, acc);
+    if constexpr (FMT == 1) {
+      if (i < 7) decode_tile_nv(p, i + 1, kn, sc_next);
+#pragma unroll
+      for (int k = 0; k < NT; ++k) acc[k] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int k = 0; k < NT; ++k) acc[k] = mfma_f16(kd[c], q[k].op[c], acc[k]);
+      sc = sc_cur;
+    } else {
+      tile_scores_n<FMT, NT>(p, q, i, sc, acc);
+    }
     if (FMT == 1) smx = __builtin_elementwise_max(smx, sc);
     else smx_mx = fmaxf(smx_mx, e8m0_to_f32(p.ks[i]));
 #pragma unroll
@@ -429,7 +459,14 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
       }
       run[k] = __builtin_fmaxf(__builtin_fmaxf(run[k], acc[k][0]), acc[k][1]);
       run[k] = __builtin_fmaxf(__builtin_fmaxf(run[k], acc[k][2]), acc[k][3]);
-      asm volatile("" : "+v"(run[k]));  // the tile is finished before the next one is decoded
+      asm volatile("" : "+v"(run[k]));  // the tile is finished before the one after next is decoded
+    }
+    if constexpr (FMT == 1) {
+      if (i < 7) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kd[c] = kn[c];
+        sc_cur = sc_next;
+      }
     }
   }
   float m0, m1 = 0.f;
