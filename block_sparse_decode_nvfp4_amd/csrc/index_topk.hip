@@ -431,6 +431,14 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
   f16x8 kd[4], kn[4];
   f16x2 sc_cur, sc_next;
   if constexpr (FMT == 1) decode_tile_nv(p, 0, kd, sc_cur);
+  // the tiles, with or without the causal mask: a block needs it only where a row's
+  // length ends inside it, and compiled into one loop the mask's compares and selects
+  // ran on every tile (a quarter of the loop's arithmetic)
+  bool any_mask = false;
+#pragma unroll
+  for (int k = 0; k < NT; ++k) any_mask |= need_mask[k];
+  auto tiles = [&](auto masked) {
+  constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     f16x2 sc;
@@ -451,7 +459,7 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
     else smx_mx = fmaxf(smx_mx, e8m0_to_f32(p.ks[i]));
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
-      if (need_mask[k]) {
+      if (MASKED && need_mask[k]) {
         const int t0 = j * kPage + 16 * i + 4 * G;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
@@ -469,6 +477,9 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
       }
     }
   }
+  };
+  if (any_mask) tiles(std::true_type{});
+  else tiles(std::false_type{});
   float m0, m1 = 0.f;
   if (FMT == 1) {
     m0 = lane_fmax<1, 16>((float)smx[0]);
