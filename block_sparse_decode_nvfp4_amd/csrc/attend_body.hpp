@@ -148,6 +148,35 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
     }
   }
 
+  // ---- query heads as the B operand, the same for all of the wave's blocks: NVFP4
+  // scaled by 2^P into fp16 range (built once here); MXFP4 the bf16 values as they are
+  typedef typename Dec::op_t op_t;
+  op_t qop[4];
+  float c = 0.f;  // logits in log2 units: x = S' * c
+  if constexpr (FMT == 1) {
+    uint32_t mx = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
+    mx = lane_max<1, 64>(mx);
+    int P = 0;
+    if (mx) {
+      const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
+      const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
+      P = 13 - fl;
+      P = P > 64 ? 64 : (P < -64 ? -64 : P);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
+        qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
+      }
+    c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
+  }
+
   float m_run = -INFINITY, l_run = 0.f;  // per head n (replicated over G)
   f32x4 o[8];
 #pragma unroll
@@ -188,47 +217,18 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
         else vs[i] = vsp[(t0 + 16 * i + n) * SB + G];
       }
 
-      // ---- query heads as the B operand: NVFP4 scaled by 2^P into fp16 range; MXFP4
-      // the bf16 values as they are
-      typedef typename Dec::op_t op_t;
-      op_t qop[4];
-      float c;  // logits in log2 units: x = S' * c
-      if constexpr (FMT == 1) {
-        uint32_t mx = 0;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
-        mx = lane_max<1, 64>(mx);
-        int P = 0;
-        if (mx) {
-          const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
-          const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
-          P = 13 - fl;
-          P = P > 64 ? 64 : (P < -64 ? -64 : P);
-        }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
-            qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
-          }
-        c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
-      } else {
+      if constexpr (FMT == 2) {  // MXFP4: the bf16 words as they are, set per block (set once before the loop, the two-block build spills)
 #pragma unroll
         for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8, raw[s]);
         c = a.sm_scale * 1.4426950408889634f;
       }
-
       // ---- S^T tiles: st[i][v] = logit of token t0 + 16 i + 4 G + v for head n
       f32x4 st[kTiles];
 #pragma unroll
       for (int i = 0; i < kTiles; ++i) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         typename Dec::scale_t s0, s1;
-        if (FMT == 1) { s0 = Dec::scale(ks[i] & 0xFFu); s1 = Dec::scale(ks[i] >> 8); }
-        else { s0 = s1 = Dec::scale(ks[i]); }
+        Dec::scales(ks[i], s0, s1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = mfma16(Dec::run(kr[i][s], s < 2 ? s0 : s1), qop[s], acc);
         st[i] = acc * c;
@@ -260,7 +260,7 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
             lsum += p;
           }
         lsum = lane_sum<16, 64>(lsum);
-        if constexpr (REPS == 1) {
+        if (REPS == 1 || rep == 0) {  // the wave's first block: nothing to rescale
           l_run = lsum;
         } else {
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // head n; 0 while m_run is -inf
@@ -284,8 +284,7 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
           for (int h4 = 0; h4 < kVChunk / 16; ++h4) {
             const int i = (kVChunk / 16) * cidx + h4;
             typename Dec::scale_t s0, s1;
-            if (FMT == 1) { s0 = Dec::scale(vs[i] & 0xFFu); s1 = Dec::scale(vs[i] >> 8); }
-            else { s0 = s1 = Dec::scale(vs[i]); }
+            Dec::scales(vs[i], s0, s1);
             _Float16* dst = &vb[16 * h4 + n][32 * G];
 #pragma unroll
             for (int s = 0; s < 4; ++s)

@@ -75,8 +75,14 @@ __device__ __forceinline__ bf16x8 fp4x8_to_bf16_pow2(uint32_t d, float p2) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// E4M3FN scale byte -> the same value in fp16 (exact: 2^-9 .. 448 are fp16 normals).
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) { return (_Float16)e4m3_to_f32(b); }
+// The two E4M3FN bytes in the low 16 bits of w as fp16 (byte 0 in element 0), in one
+// hardware conversion: gfx950's fp8 conversion reads OCP E4M3FN, subnormals included, and
+// every value it gives (2^-9 .. 448) converts to fp16 exactly, so the rounding mode of
+// the narrowing does not matter.
+__device__ __forceinline__ f16x2 e4m3x2_to_f16x2(uint32_t w) {
+  const auto sf = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  return __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(sf[0], sf[1]));
+}
 
 // 8 codes of one dword times an E4M3 scale, as fp16 (exact).
 __device__ __forceinline__ f16x8 fp4x8_to_f16_e4m3(uint32_t d, _Float16 s) {
@@ -91,18 +97,27 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16_e4m3(uint32_t d, _Float16 s) {
 // E8M0 byte. op_t is the MFMA operand of 8 decoded elements.
 template <int FMT>
 struct Decode;
+// scales(w, s0, s1): the scales of a lane's two 16-dim halves of its 32 dims, from the
+// scale bytes it loaded (NVFP4: two E4M3 bytes, one per 16-element group; MXFP4: one E8M0
+// byte for the whole 32-element group).
 template <>
 struct Decode<1> {  // NVFP4: scale byte is E4M3FN
   typedef _Float16 scale_t;
   typedef f16x8 op_t;
-  static __device__ __forceinline__ scale_t scale(uint32_t byte) { return e4m3_to_f16(byte); }
+  static __device__ __forceinline__ void scales(uint32_t w, scale_t& s0, scale_t& s1) {
+    const f16x2 s = e4m3x2_to_f16x2(w);
+    s0 = s[0];
+    s1 = s[1];
+  }
   static __device__ __forceinline__ op_t run(uint32_t d, scale_t s) { return fp4x8_to_f16_e4m3(d, s); }
 };
 template <>
 struct Decode<2> {  // MXFP4: scale byte is E8M0
   typedef float scale_t;
   typedef bf16x8 op_t;
-  static __device__ __forceinline__ scale_t scale(uint32_t byte) { return e8m0_to_f32(byte); }
+  static __device__ __forceinline__ void scales(uint32_t w, scale_t& s0, scale_t& s1) {
+    s0 = s1 = e8m0_to_f32(w);
+  }
   static __device__ __forceinline__ op_t run(uint32_t d, scale_t s) { return fp4x8_to_bf16_pow2(d, s); }
 };
 

@@ -226,6 +226,51 @@ def test_attend_mxfp4_extreme_scales(gpu):
     assert worst <= TOL, worst
 
 
+def test_attend_nvfp4_scale_range(gpu):
+    """NVFP4 K / V groups over the E4M3 scale range: request 0 scaled by 2^-7 (most groups
+    take subnormal scales, below 2^-6), request 1 by 2^6 (the outlier groups' scales near
+    the 448 top), request 2 by 2^e per 128-token block (K) and per 64 tokens (V), e cycling
+    over -8 .. 6. The attention decodes code x scale exactly in fp16 for every E4M3 byte and
+    matches the oracle within 5e-3, through the split kernel (the oracle's ids) and through
+    the one-call top-k + attention (its own ids, bit-exact)."""
+    case = W.make_case(CFG0, DEV, seq_lens=[3000, 2500, 2600], q_len=2, G=16)
+    lay = case.layout
+    n = case.k.shape[0]
+    tok = torch.arange(n, device=DEV)
+    req = torch.bucketize(tok, torch.as_tensor(lay.tok_off[1:], device=DEV), right=True)
+    loc = tok - torch.as_tensor(lay.tok_off, device=DEV)[req]
+    e_k = torch.where(req == 0, -7, torch.where(req == 1, 6, (loc // 128) % 15 - 8)).to(torch.float32)
+    e_v = torch.where(req == 0, -7, torch.where(req == 1, 6, (loc // 64) % 15 - 8)).to(torch.float32)
+    case.k = (case.k.float() * torch.exp2(e_k)[:, None]).to(torch.bfloat16)
+    case.v = (case.v.float() * torch.exp2(e_v)[:, None]).to(torch.bfloat16)
+    sm = 2.0 ** -6   # logits of order one for the 2^6-scaled keys
+    step = run_gpu_step(gpu, CFG0, DEV, topk=8, fmt="nvfp4", case=case, sm_scale=sm)
+    assert step.status == 0, hex(step.status)
+    sc = step.cache.planes["k"][1].cpu().numpy().ravel()
+    sv = step.cache.planes["v"][1].cpu().numpy().ravel()
+    for p in (sc, sv):
+        mag = p & 0x7F
+        assert ((mag >= 1) & (mag <= 7)).any() and (mag >= 0x76).any()   # subnormal and near 448
+    R = step.rows.num_rows
+    ids, outs, _, _ = oracle_requests(step, "nvfp4", 8, sm, range(3))
+    got, st = _attend(gpu, step, _oracle_ids_matrix(ids, R, 8), sm)
+    assert st == 0
+    worst = max(max_rel_err(got[r], want) for r, want in outs.items())
+    assert worst <= TOL, worst
+    ws = gpu.index_attend_workspace(step.rows, lay.max_blocks, 8, 16, DEV)
+    fid = torch.full((R, 8), -9, dtype=torch.int32, device=DEV)
+    fout = torch.full((R, 16, 128), float("nan"), dtype=torch.float32, device=DEV)
+    st2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gpu.m3s_index_topk_attend(step.cache, case.q_idx, case.q, step.bt, lay.max_blocks, step.rows, 8, sm,
+                              topk_ids=fid, out=fout, workspace=ws, dev_status=st2)
+    torch.cuda.synchronize()
+    assert int(st2.item()) == 0
+    fid, fout = fid.cpu().numpy(), fout.cpu().double().numpy()
+    for r, want in outs.items():
+        assert (fid[r] == np.asarray(ids[r])).all(), r
+        assert max_rel_err(fout[r], want) <= TOL, r
+
+
 def test_attend_mxfp4_unstorable_scale_flagged(gpu):
     """An E8M0 scale byte above 252 (no store writes one) decodes to infinity: the
     affected outputs are written as 0 and the range bit is set; nothing is NaN."""
