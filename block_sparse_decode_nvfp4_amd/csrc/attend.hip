@@ -7,8 +7,8 @@
 //
 // split kernel - workgroup (row, split), 8 waves, two per selected block, each
 //   taking 64 of its tokens (so a split covers 4 of the row's k blocks; with
-//   many more split workgroups than fit the GPU at once, each wave takes two
-//   blocks in turn and a split covers 8). Per wave and block:
+//   many more split workgroups than fit the GPU at once, each wave takes two or
+//   four blocks in turn and a split covers 8 or 16). Per wave and block:
 //     S^T = K Q^T on 16-bit MFMA (K tile of 16 tokens as A, the G <= 16
 //       query heads as B); K is decoded exactly (NVFP4 to fp16, MXFP4 to
 //       bf16).
@@ -27,8 +27,8 @@
 
 namespace m3s {
 
-// Two blocks per wave are kept to four waves per SIMD (128 VGPRs), so two
-// workgroups still share a CU.
+// Two or four blocks per wave are kept to four waves per SIMD (128 VGPRs), so
+// two workgroups still share a CU.
 template <int FMT, int REPS>
 __global__ __launch_bounds__(kWaves * 64, REPS == 1 ? 1 : 4) void attend_split_kernel(AttendArgs a) {
   __shared__ AttendShared sh;
@@ -107,7 +107,12 @@ size_t attend_ws_bytes(int32_t num_rows, int32_t nsplit) {
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream) {
   if (a.num_rows == 0) return hipSuccess;
   const unsigned grid = (unsigned)((int64_t)a.num_rows * a.nsplit);
-  if (a.reps == 2) {
+  if (a.reps == 4) {
+    if (a.format == 1)
+      hipLaunchKernelGGL((attend_split_kernel<1, 4>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attend_split_kernel<2, 4>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
+  } else if (a.reps == 2) {
     if (a.format == 1)
       hipLaunchKernelGGL((attend_split_kernel<1, 2>), dim3(grid), dim3(kWaves * 64), 0, stream, a);
     else

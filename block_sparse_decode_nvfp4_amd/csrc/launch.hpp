@@ -144,7 +144,7 @@ struct AttendArgs {
   int32_t topk;
   int32_t nsplit;
   int32_t xcd_rows;  // nonzero: the split kernel deals a row's splits to one XCD
-  int32_t reps;      // blocks each split-kernel wave attends in turn (1 or 2)
+  int32_t reps;      // blocks each split-kernel wave attends in turn (1, 2 or 4)
   float sm_scale;
   float* out;
   float* part_o;   // [num_rows, nsplit, 16, 128]
