@@ -382,17 +382,14 @@ m3s_status attend_args(AttendArgs& a, const m3s_cache* cache, const uint16_t* q,
   // L2; measured faster while every split workgroup is resident at once (64 rows:
   // 14.9 -> 14.1 us), slightly slower with several rounds of workgroups (384 rows).
   a.xcd_rows = rows->num_rows > 0 && (int64_t)rows->num_rows * nsplit <= 2 * (int64_t)scan_grid() ? 1 : 0;
-  // With more than two rounds of split workgroups, each wave attends two blocks
-  // in turn (online softmax across them): half the splits, so half the partials
-  // written and combined; with more than four rounds, four blocks in turn (a
-  // top-k of 16 is then one split per row: no partials and no combine). Either way
-  // at least two rounds of workgroups remain. The workspace stays sized for the
+  // With more than two rounds of split workgroups, each wave attends four blocks
+  // in turn (online softmax across them), or two when k <= 12: a quarter (half) of
+  // the splits, so fewer partials written and combined, and a top-k of 16 is one
+  // split per row with no combine at all. The workspace stays sized for the
   // one-block split count.
   a.reps = 1;
-  if (nsplit > 1 && rows->num_rows > 0) {
-    const int64_t wgs = (int64_t)rows->num_rows * nsplit, cus = scan_grid();
-    if (wgs > 8 * cus && nsplit >= 4) a.reps = 4;
-    else if (wgs > 4 * cus) a.reps = 2;
+  if (nsplit > 1 && rows->num_rows > 0 && (int64_t)rows->num_rows * nsplit > 4 * (int64_t)scan_grid()) {
+    a.reps = nsplit >= 4 ? 4 : 2;
     a.nsplit = (nsplit + a.reps - 1) / a.reps;
   }
   a.sm_scale = sm_scale;

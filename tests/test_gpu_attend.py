@@ -123,31 +123,30 @@ def test_attend_workspace_reuse(gpu, topk):
         assert torch.equal(out, step.out), rep
 
 
-def _many_row_case(topk, G, seed_shift=0, reps=2):
-    """Enough short requests of 8 rows that rows x splits exceed four (reps 2) or eight
-    (reps 4) times the CU count: the attention's split kernel then takes two or four
-    blocks per wave (online softmax across them) and a half or a quarter of the splits."""
+def _many_row_case(topk, G, seed_shift=0):
+    """Enough short requests of 8 rows that rows x splits exceed four times the CU count:
+    the attention's split kernel then takes four blocks per wave (k >= 13), or two (k <= 12),
+    with an online softmax across them, and a quarter or half of the splits."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nsplit = (topk + 3) // 4
-    rows_needed = (4 if reps == 2 else 8) * cus // nsplit + 1
+    rows_needed = 4 * cus // nsplit + 1
     lens = [300, 2048, 5000, 129, 9000, 700, 3333, 1280]
     nreq = (rows_needed + 7) // 8 + 1
     seq = [lens[(i + seed_shift) % len(lens)] + 17 * i for i in range(nreq)]
     return W.make_case(CFG0, DEV, seq_lens=seq, q_len=8, G=G), nsplit, cus
 
 
-@pytest.mark.parametrize("fmt,topk,reps", [("nvfp4", 5, 2), ("nvfp4", 12, 2), ("nvfp4", 16, 2), ("nvfp4", 20, 2),
-                                           ("nvfp4", 64, 2), ("mxfp4", 12, 2), ("nvfp4", 16, 4),
-                                           ("nvfp4", 20, 4), ("nvfp4", 64, 4), ("mxfp4", 16, 4)])
-def test_attend_two_blocks_per_wave(gpu, fmt, topk, reps):
-    """Many rows (two or four blocks per attention wave) against the oracle, including
-    top-k values whose last split leaves block slots empty (5, 12, 20), a top-k of 16 in one
-    split with four blocks per wave (no combine), and a 16-split top-k with its combine (64)."""
-    case, nsplit, cus = _many_row_case(topk, 16, reps=reps)
+@pytest.mark.parametrize("fmt,topk", [("nvfp4", 5), ("nvfp4", 12), ("mxfp4", 12), ("nvfp4", 16), ("nvfp4", 20),
+                                      ("nvfp4", 64), ("mxfp4", 16)])
+def test_attend_two_blocks_per_wave(gpu, fmt, topk):
+    """Many rows (two blocks per attention wave for k = 5 and 12, four for 16, 20 and 64)
+    against the oracle, including top-k values whose last split leaves block slots empty
+    (5, 12, 20), a top-k of 16 in one split (no combine), and a 64 in four splits with their
+    combine."""
+    case, nsplit, cus = _many_row_case(topk, 16)
     step = run_gpu_step(gpu, CFG0, DEV, topk=topk, fmt=fmt, case=case, sm_scale=0.37)
     R = step.rows.num_rows
-    assert R * nsplit > (4 if reps == 2 else 8) * cus
-    assert reps == 2 or nsplit >= 4
+    assert R * nsplit > 4 * cus
     assert step.status == 0
     ids, outs, _, _ = oracle_requests(step, fmt, topk, 0.37, range(len(case.layout.seq_lens)))
     got, st = _attend(gpu, step, _oracle_ids_matrix(ids, R, topk), 0.37)
@@ -156,19 +155,18 @@ def test_attend_two_blocks_per_wave(gpu, fmt, topk, reps):
     assert worst <= TOL, worst
 
 
-@pytest.mark.parametrize("reps", [2, 4])
-def test_attend_two_blocks_per_wave_flags_and_wide_queries(gpu, reps):
-    """Two or four blocks per wave with invalid ids (past the row's blocks, past max_blocks), a
-    block-table entry outside the cache, and queries spanning a wide range with a sharp
-    softmax: invalid blocks are skipped and flagged, and the rest matches the oracle over
-    the valid blocks."""
-    topk = 16
-    case, nsplit, cus = _many_row_case(topk, 16, seed_shift=3, reps=reps)
+@pytest.mark.parametrize("topk", [12, 16])
+def test_attend_two_blocks_per_wave_flags_and_wide_queries(gpu, topk):
+    """Two (k = 12) or four (k = 16) blocks per wave with invalid ids (past the row's blocks,
+    past max_blocks), a block-table entry outside the cache, and queries spanning a wide range
+    with a sharp softmax: invalid blocks are skipped and flagged, and the rest matches the
+    oracle over the valid blocks."""
+    case, nsplit, cus = _many_row_case(topk, 16, seed_shift=3)
     case.q[0::5, :8] *= 64
     case.q[1::7, 8:] *= 2.0 ** -20
     step = run_gpu_step(gpu, CFG0, DEV, topk=topk, case=case, sm_scale=2.0)
     R = step.rows.num_rows
-    assert R * nsplit > (4 if reps == 2 else 8) * cus and step.status == 0
+    assert R * nsplit > 4 * cus and step.status == 0
     lay = case.layout
     ids, outs, _, rl = oracle_requests(step, "nvfp4", topk, 2.0, range(len(lay.seq_lens)))
     m = _oracle_ids_matrix(ids, R, topk)
