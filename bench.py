@@ -32,7 +32,7 @@ MFMA_PEAK_TFLOPS = {"f16": 2500.0, "fp8": 5000.0}  # dense, MI355X
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["block_sparse_decode_nvfp4_amd/csrc/" + f for f in (
     "index_topk.hip", "attend_body.hpp", "attend.hip", "store.hip", "rows.hip", "rows_body.hpp", "quant.hpp",
-    "fp4.hpp", "launch.hpp", "store_body.hpp")]
+    "fp4.hpp", "launch.hpp", "store_body.hpp", "api.cpp")]   # api.cpp: the launch choices
 
 
 def traffic_file(workload):
