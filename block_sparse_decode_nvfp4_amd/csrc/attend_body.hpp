@@ -248,8 +248,14 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
       // a wave's 64 tokens can all lie past the row's length: it then stays empty
       if (tok_base < len) {
         // mx_l is finite: the wave's tokens include a causal one. Over several
-        // blocks the running sum and O are rescaled to the new running max.
-        const float m_new = REPS == 1 ? mx_l : fmaxf(m_run, mx_l);
+        // blocks the running sum and O are rescaled to a new running max, but only
+        // when some head's block maximum exceeds its running max by more than 2^8:
+        // otherwise the running max stays (the weights are then below 2^8, in range
+        // for the 16-bit P operand, and the sums are the same up to rounding) and the
+        // rescale is skipped. The decision is the wave's, so O is rescaled for all
+        // heads or none.
+        const bool grow = REPS == 1 || rep == 0 || __builtin_amdgcn_ballot_w64(mx_l > m_run + 8.f) != 0;
+        const float m_new = REPS == 1 ? mx_l : (grow ? fmaxf(m_run, mx_l) : m_run);
         float lsum = 0.f;
 #pragma unroll
         for (int i = 0; i < kTiles; ++i)
@@ -262,6 +268,8 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
         lsum = lane_sum<16, 64>(lsum);
         if (REPS == 1 || rep == 0) {  // the wave's first block: nothing to rescale
           l_run = lsum;
+        } else if (!grow) {
+          l_run += lsum;
         } else {
           const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // head n; 0 while m_run is -inf
           l_run = l_run * alpha + lsum;
