@@ -185,10 +185,29 @@ __device__ __forceinline__ double lane_xor(double x) {
 
 // Butterfly reductions over the lanes whose index differs in bits LO..HI-1
 // (e.g. <1, 16>: the 16 lanes of a row; <16, 64>: the four rows; <1, 64>: all).
+// op must be commutative: at M = 16 and 32 the permlane swap hands every lane its own
+// value and its partner's, in an order that depends on the lane, and op takes the two
+// as they come (no select of the partner's half). A lane whose bit M is clear gets
+// op(own, partner), as through lane_xor.
 template <int LO, int HI, typename T, typename F>
 __device__ __forceinline__ T lane_reduce(T x, F op) {
   if constexpr (LO < HI) {
-    x = op(x, lane_xor<LO>(x));
+    if constexpr ((LO == 16 || LO == 32) && sizeof(T) == 4) {
+      const uint32_t u = __builtin_bit_cast(uint32_t, x);
+      uint32_t a, b;
+      if constexpr (LO == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        a = r[0];
+        b = r[1];
+      } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        a = r[0];
+        b = r[1];
+      }
+      x = op(__builtin_bit_cast(T, a), __builtin_bit_cast(T, b));
+    } else {
+      x = op(x, lane_xor<LO>(x));
+    }
     return lane_reduce<LO * 2, HI>(x, op);
   } else {
     return x;
