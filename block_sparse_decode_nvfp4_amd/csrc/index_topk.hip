@@ -373,6 +373,42 @@ __device__ __forceinline__ f32x4 tile_scores(const PageBuf& p, const QueryTile& 
   return acc;
 }
 
+// Largest of each half of a packed fp16 pair over the 16 lanes of a row (one packed max
+// per exchange instead of two fp32 reductions).
+__device__ __forceinline__ f16x2 row_max_f16x2(f16x2 v) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  u = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(f16x2, u),
+                                                              __builtin_bit_cast(f16x2, lane_xor_u32<1>(u))));
+  u = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(f16x2, u),
+                                                              __builtin_bit_cast(f16x2, lane_xor_u32<2>(u))));
+  u = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(f16x2, u),
+                                                              __builtin_bit_cast(f16x2, lane_xor_u32<4>(u))));
+  u = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(f16x2, u),
+                                                              __builtin_bit_cast(f16x2, lane_xor_u32<8>(u))));
+  return __builtin_bit_cast(f16x2, u);
+}
+
+// Four per-lane values x[k] reduced over the wave's four rows (op commutative), so that
+// row G ends with the result for k = G: a reduce-scatter of two swap steps (three swaps,
+// three ops) instead of a butterfly per value. The permlane32 swap exchanges the upper
+// half of its first operand with the lower half of its second, the permlane16 swap the
+// odd rows of its first with the even rows of its second.
+template <typename F>
+__device__ __forceinline__ float rows_reduce_scatter4(float x0, float x1, float x2, float x3, F op) {
+  const float x[4] = {x0, x1, x2, x3};
+  auto swap32 = [](float a, float b, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+  };
+  float a0, a1, b0, b1;
+  swap32(x[0], x[2], a0, a1);  // lanes 0-31: x[0] of rows 0-1 and of rows 2-3; lanes 32-63: x[2]
+  swap32(x[1], x[3], b0, b1);  // the same for x[1] / x[3]
+  const float m02 = op(a0, a1), m13 = op(b0, b1);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(m02), __float_as_uint(m13), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Score one page against the request's rows; write the fp32 score and error bound.
 template <int FMT>
 __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q, const IndexArgs& a, int j, int n,
@@ -399,7 +435,8 @@ __device__ __forceinline__ void score_page(const PageBuf& p, const QueryTile& q,
   run = lane_fmax<16, 64>(run);
   float part;
   if (FMT == 1) {
-    const float m0 = lane_fmax<1, 16>((float)smx[0]), m1 = lane_fmax<1, 16>((float)smx[1]);
+    const f16x2 sm = row_max_f16x2(smx);
+    const float m0 = (float)sm[0], m1 = (float)sm[1];
     part = 6.0f * (m0 * (kAccRel * q.qs0 + q.qe0) + m1 * (kAccRel * q.qs1 + q.qe1));
   } else {
     const float m0 = lane_fmax<1, 16>(smx_mx);
@@ -482,10 +519,42 @@ __device__ __forceinline__ void score_page_n(const PageBuf& p, const QueryTile (
   else tiles(std::false_type{});
   float m0, m1 = 0.f;
   if (FMT == 1) {
-    m0 = lane_fmax<1, 16>((float)smx[0]);
-    m1 = lane_fmax<1, 16>((float)smx[1]);
+    const f16x2 sm = row_max_f16x2(smx);
+    m0 = (float)sm[0];
+    m1 = (float)sm[1];
   } else {
     m0 = lane_fmax<1, 16>(smx_mx);
+  }
+  if constexpr (NT == 4) {
+    // row G of the wave finishes tile k = G: its maxima and bound terms reduce-scattered
+    // over the rows, then one score and one bound store per lane
+    float part[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      part[k] = FMT == 1 ? 6.0f * (m0 * (kAccRel * q[k].qs0 + q[k].qe0) + m1 * (kAccRel * q[k].qs1 + q[k].qe1))
+                         : 6.0f * m0 * (kAccRel * q[k].qs0 + q[k].qe0);
+    const float r = rows_reduce_scatter4(run[0], run[1], run[2], run[3],
+                                         [](float x, float y) { return __builtin_fmaxf(x, y); });
+    const float b = rows_reduce_scatter4(part[0], part[1], part[2], part[3], [](float x, float y) { return x + y; });
+    // tile G's row fields; each candidate is pinned so that the choice stays a chain of
+    // selects (folded into an index into the tile array it would put the tiles in scratch)
+    float uns = q[0].unscale;
+    int r0 = q[0].r0, ql = q[0].ql;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      float u = q[k].unscale;
+      int rk = q[k].r0, qk = q[k].ql;
+      asm volatile("" : "+v"(u), "+v"(rk), "+v"(qk));
+      uns = G == k ? u : uns;
+      r0 = G == k ? rk : r0;
+      ql = G == k ? qk : ql;
+    }
+    if (n < ql) {
+      const int64_t o = (int64_t)(r0 + n) * a.max_blocks + j;
+      a.ws_score[o] = r * uns;
+      a.ws_bound[o] = b * uns * (1.0f + 0x1p-10f);
+    }
+    return;
   }
 #pragma unroll
   for (int k = 0; k < NT; ++k) {
