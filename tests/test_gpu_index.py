@@ -58,11 +58,13 @@ def test_index_zero_query_ties(gpu, tie_high):
         assert all(row == want for row in step.ids.cpu().numpy().tolist())
 
 
-def test_index_equal_blocks_need_exact_rescore(gpu):
+@pytest.mark.parametrize("fmt,q_len", [("nvfp4", 2), ("nvfp4", 70), ("mxfp4", 70)])
+def test_index_equal_blocks_need_exact_rescore(gpu, fmt, q_len):
     """Every page holds the same tokens, so every block ties exactly but the fp32 error
     bound is non-zero: the band covers all blocks and the exact rescore must order them
-    by id."""
-    case = W.make_case(CFG0, DEV, seq_lens=[128 * 40, 128 * 33 + 5], q_len=2, G=2)
+    by id. With 70 rows per request the rows go through the prefill row map and the wide
+    scan (two 64-row work groups per request, the second partly filled)."""
+    case = W.make_case(CFG0, DEV, seq_lens=[128 * 40, 128 * 33 + 5], q_len=q_len, G=2)
     lay = case.layout
     for b in range(2):
         lo, hi = int(lay.tok_off[b]), int(lay.tok_off[b + 1])
@@ -70,9 +72,9 @@ def test_index_equal_blocks_need_exact_rescore(gpu):
         base = case.idx[lo: lo + 128].clone()
         reps = (n + 127) // 128
         case.idx[lo:hi] = base.repeat(reps, 1)[:n]
-    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case, fmt=fmt, prefill=q_len > 16)
     assert step.status == 0, hex(step.status)
-    _check_all(gpu, step, "nvfp4", 16)
+    _check_all(gpu, step, fmt, 16)
 
 
 def test_index_band_overflow_selects_by_key(gpu):
@@ -99,10 +101,13 @@ def test_index_band_overflow_selects_by_key(gpu):
     assert torch.equal(ids_f, step.ids)
 
 
-def test_index_near_ties_are_decided_exactly(gpu):
+@pytest.mark.parametrize("fmt,q_len", [("nvfp4", 4), ("nvfp4", 70), ("mxfp4", 70)])
+def test_index_near_ties_are_decided_exactly(gpu, fmt, q_len):
     """Blocks that differ from block 0 by a single tiny element: exact scores differ far
-    below the fp32 error bound, so the selection is decided by the float64 rescore."""
-    case = W.make_case(CFG0, DEV, seq_lens=[128 * 64], q_len=4, G=2)
+    below the fp32 error bound, so the selection is decided by the float64 rescore (70
+    rows: the prefill row map and the wide scan, whose bounds are reduced across the
+    wave's rows for four query tiles at once)."""
+    case = W.make_case(CFG0, DEV, seq_lens=[128 * 64], q_len=q_len, G=2)
     n = 128 * 64
     base = case.idx[:128].clone()
     idx = base.repeat(64, 1)
@@ -113,9 +118,9 @@ def test_index_near_ties_are_decided_exactly(gpu):
         d = int(torch.randint(0, 128, (1,), generator=g))
         idx[t, d] = (idx[t, d].float() * (1 + 2.0 ** -7 * int(torch.randint(-2, 3, (1,), generator=g)))).to(torch.bfloat16)
     case.idx[:n] = idx
-    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case)
+    step = run_gpu_step(gpu, CFG0, DEV, topk=16, case=case, fmt=fmt, prefill=q_len > 16)
     assert step.status == 0, hex(step.status)
-    _check_all(gpu, step, "nvfp4", 16)
+    _check_all(gpu, step, fmt, 16)
 
 
 def test_index_fewer_blocks_than_k(gpu):
