@@ -1036,7 +1036,7 @@ __device__ __forceinline__ uint64_t sort_desc_first(uint64_t x, int n) {
 //      it does not exactly fill the open slots each band block is rescored in
 //      exact float64 by one wave, over only the tokens its bound leaves open;
 //   3. the k selected ids are gathered in LDS and one wave sorts them ascending.
-// Score registers per thread: PER = 5, 8, 16 or 32 (rows of up to 256 PER blocks),
+// Score registers per thread: PER = 5, 8, 14, 16 or 32 (rows of up to 256 PER blocks),
 // picked at launch from max_blocks; the smallest that fits keeps the kernel's
 // code small (it runs once per row on cold instruction caches).
 
@@ -1551,12 +1551,14 @@ static void launch_select_fmt(const IndexArgs& a, hipStream_t stream) {
       if (a.num_rows > 2 * (int64_t)a.scan_grid) {
         if (a.max_blocks <= 256 * 5) launch_select_as<FMT, 5, 3>(a, stream);
         else if (a.max_blocks <= 256 * 8) launch_select_as<FMT, 8, 3>(a, stream);
+        else if (a.max_blocks <= 256 * 14) launch_select_as<FMT, 14, 3>(a, stream);
         else launch_select_as<FMT, 16, 3>(a, stream);
         return;
       }
     }
     if (a.max_blocks <= 256 * 5) launch_select_as<FMT, 5, 1>(a, stream);
     else if (a.max_blocks <= 256 * 8) launch_select_as<FMT, 8, 1>(a, stream);
+    else if (a.max_blocks <= 256 * 14) launch_select_as<FMT, 14, 1>(a, stream);
     else launch_select_as<FMT, 16, 1>(a, stream);
   } else {
     launch_select_as<FMT, 32, 1>(a, stream);
@@ -1595,6 +1597,9 @@ static hipError_t launch_select_attend_after_scan(const IndexArgs& ia, const Att
   } else if (ia.max_blocks <= 256 * 8) {
     if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 8>), g, blk, 0, stream, ia, aa);
     else hipLaunchKernelGGL((select_attend_kernel<2, 8>), g, blk, 0, stream, ia, aa);
+  } else if (ia.max_blocks <= 256 * 14) {
+    if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 14>), g, blk, 0, stream, ia, aa);
+    else hipLaunchKernelGGL((select_attend_kernel<2, 14>), g, blk, 0, stream, ia, aa);
   } else if (ia.max_blocks <= 256 * 16) {
     if (ia.format == 1) hipLaunchKernelGGL((select_attend_kernel<1, 16>), g, blk, 0, stream, ia, aa);
     else hipLaunchKernelGGL((select_attend_kernel<2, 16>), g, blk, 0, stream, ia, aa);

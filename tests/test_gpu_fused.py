@@ -78,6 +78,9 @@ ORACLE_CASES = [
     ("mxfp4", [30_000, 700], 4, 3, 16),                 # G not a power of two
     ("nvfp4", [500_000], 2, 2, 16),                     # 3907 blocks: 16 per thread
     ("mxfp4", [1_000_000], 2, 2, 16),                   # 7813 blocks: 32 per thread
+    ("mxfp4", [400_000, 3000], 2, 4, 16),               # 3125 blocks: 14 per thread
+    ("nvfp4", [300_000], 3, 4, 16),                     # 2344 blocks: 14 per thread
+    ("mxfp4", [150_000, 900], 2, 4, 16),                # 1172 blocks: 5 per thread
 ]
 
 
