@@ -183,7 +183,8 @@ def cpu_baseline(cfg, case, nreq, log_fn):
 COPY_BYTES = 1 << 30          # the calibration copy reads and writes this many bytes
 
 
-FRONT_KERNELS = ("store_rows_kernel", "store_kernel", "decode_rows_kernel", "prefill_rows_kernel")
+FRONT_KERNELS = ("store_rows_kernel", "store_prefill_rows_kernel", "store_kernel", "decode_rows_kernel",
+                 "prefill_rows_kernel")
 STEP_OPENERS = FRONT_KERNELS + ("step_scan_kernel",)   # the first kernel of a step, in each call mode
 
 
@@ -464,7 +465,7 @@ def main():
     ap.add_argument("--stage-reps", type=int, default=20)
     ap.add_argument("--calls", choices=("step", "two", "separate"), default="step",
                     help="step: one m3s_decode_step call (decode workloads; a prefill chunk runs 'two'); "
-                         "two: m3s_store_and_rows (decode) or m3s_store + m3s_prefill_rows (prefill), then "
+                         "two: m3s_store_and_rows (decode) or m3s_store_and_prefill_rows (prefill), then "
                          "m3s_index_topk_attend; separate: m3s_store, the row map, m3s_index_topk, "
                          "m3s_sparse_attend")
     ap.add_argument("--separate", action="store_true", help="same as --calls separate")
@@ -575,6 +576,9 @@ def main():
             return
         if fused_front:
             m3s.m3s_store_and_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, row_req, row_len, req_blk, status)
+        elif prefill and calls != "separate":
+            m3s.m3s_store_and_prefill_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, rows.num_groups, status,
+                                           out=rows)
         else:
             m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
             row_map()
@@ -682,14 +686,22 @@ def main():
     # the layer caches), between two events on the stream it runs on; a GPU spin first lets
     # every launch queue up before the GPU reaches it, so no host launch gap lands inside
     # and the events' own cost is spread over the repetitions.
+    fused_prefill_front = prefill and calls != "separate"
+
     def front(c):
         if fused_front:
             m3s.m3s_store_and_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, row_req, row_len, req_blk, status)
+        elif fused_prefill_front:
+            m3s.m3s_store_and_prefill_rows(c, k_new, v_new, i_new, s_new, cu_q, seq, R, rows.num_groups, status,
+                                           out=rows)
         else:
             m3s.m3s_store(c, k_new, v_new, i_new, s_new, status)
             row_map()
 
-    stages = [("store_and_rows" if fused_front else ("store+prefill_rows" if prefill else "store+decode_rows"), front),
+    front_name = ("store_and_rows" if fused_front else
+                  "store_and_prefill_rows" if fused_prefill_front else
+                  "store+prefill_rows" if prefill else "store+decode_rows")
+    stages = [(front_name, front),
               ("index_topk", lambda c: m3s.m3s_index_topk(c, case.q_idx, bt, lay.max_blocks, rows, cfg.topk, 0,
                                                            ids, ws_i, status)),
               ("sparse_attend", lambda c: m3s.m3s_sparse_attend(c, case.q, bt, lay.max_blocks, rows, ids,
@@ -832,7 +844,7 @@ def main():
                    "context": [int(x) for x in sorted(set(lay.seq_lens.tolist()))][:4],
                    "heads_per_kv_head": G, "topk": cfg.topk, "cache_format": cfg.fmt, "layers_cycled": NL,
                    "calls": {"step": "m3s_decode_step",
-                             "two": ("m3s_store + m3s_prefill_rows" if prefill else "m3s_store_and_rows") +
+                             "two": ("m3s_store_and_prefill_rows" if prefill else "m3s_store_and_rows") +
                                     ", m3s_index_topk_attend",
                              "separate": "m3s_store, " + ("m3s_prefill_rows" if prefill else "m3s_decode_rows") +
                                          ", m3s_index_topk, m3s_sparse_attend"}[calls]},

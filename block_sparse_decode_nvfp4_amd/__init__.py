@@ -7,6 +7,7 @@ the path runs in the library's HIP kernels. Loading fails loudly when the
 library is missing: there is no fallback.
 
 Functions carry the C names: m3s_store, m3s_decode_rows, m3s_store_and_rows, m3s_prefill_rows,
+m3s_store_and_prefill_rows,
 m3s_qknorm_rope_store, m3s_index_topk, m3s_sparse_attend, m3s_index_topk_attend, m3s_decode_step,
 m3s_workspace_bytes,
 m3s_read_device_status, m3s_status_string, m3s_version.
@@ -34,7 +35,8 @@ DEV_BITS = {
     "RANGE": 1 << 8, "STEP_SLOT": 1 << 9,
 }
 
-EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_qknorm_rope_store",
+EXPORTS = ("m3s_store", "m3s_decode_rows", "m3s_store_and_rows", "m3s_prefill_rows", "m3s_store_and_prefill_rows",
+           "m3s_qknorm_rope_store",
            "m3s_index_topk", "m3s_sparse_attend", "m3s_index_topk_attend",
            "m3s_workspace_bytes", "m3s_read_device_status", "m3s_status_string", "m3s_version",
            "m3s_probe_page_reads", "m3s_index_topk_attend_noalloc", "m3s_decode_step")
@@ -85,6 +87,7 @@ def load(path: str | None = None):
         "m3s_decode_rows": (I32, [V, V, I32, I32, V, V, V, V, V]),
         "m3s_prefill_rows": (I32, [V, V, I32, I32, I32, V, V, V, V, V, V, V]),
         "m3s_store_and_rows": (I32, [V, V, V, V, I64, V, I32, V, V, I32, I32, V, V, V, V, V]),
+        "m3s_store_and_prefill_rows": (I32, [V, V, V, V, I64, V, I32, V, V, I32, I32, I32, V, V, V, V, V, V, V]),
         "m3s_qknorm_rope_store": (I32, [V, V, I64, I32, V, V, V, V, I64, V, F32, V, V, I32, I32, V, I32,
                                         V, V, V, V, V]),
         "m3s_index_topk": (I32, [V, V, I64, V, I32, I32, V, I32, I32, I32, I32, V, V, SZ, V, V]),
@@ -305,11 +308,7 @@ def m3s_store_and_rows(cache: Cache, k, v, idx, slot_mapping, cu_q, seq_lens, nu
     return Rows(cu_q, None, req_blk, row_req, row_len, B, num_rows)
 
 
-def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = None, dev_status=None,
-                     stream=None, out: Rows | None = None) -> Rows:
-    """Prefill row map and 64-row scan groups; max_groups defaults to the bound
-    ceil(num_rows / 64) + num_reqs (capped at MAX_GROUPS). ``out`` (a Rows from an
-    earlier call with the same sizes) is written in place."""
+def _prefill_rows_out(cu_q, seq_lens, num_rows, max_groups, out):
     torch = _torch()
     _need(cu_q, "cu_q", torch.int32)
     _need(seq_lens, "seq_lens", torch.int32)
@@ -322,18 +321,52 @@ def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = Non
     if out is not None:
         if out.num_groups != max_groups or out.num_rows != num_rows:
             raise ValueError("out was made for other sizes")
-        row_req, row_len, grp_row, grp_req, grp_blk = out.row_req, out.row_len, out.grp_row, out.grp_req, out.grp_blk
-    else:
-        row_req = torch.empty(num_rows, dtype=torch.int32, device=dev)
-        row_len = torch.empty(num_rows, dtype=torch.int32, device=dev)
-        grp_row = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
-        grp_req = torch.empty(max_groups, dtype=torch.int32, device=dev)
-        grp_blk = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
-    st = load().m3s_prefill_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, max_groups, _ptr(row_req),
-                                 _ptr(row_len), _ptr(grp_row), _ptr(grp_req), _ptr(grp_blk), _ptr(dev_status),
-                                 _stream(stream))
+        return B, max_groups, out
+    row_req = torch.empty(num_rows, dtype=torch.int32, device=dev)
+    row_len = torch.empty(num_rows, dtype=torch.int32, device=dev)
+    grp_row = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
+    grp_req = torch.empty(max_groups, dtype=torch.int32, device=dev)
+    grp_blk = torch.empty(max_groups + 1, dtype=torch.int32, device=dev)
+    return B, max_groups, Rows(grp_row, grp_req, grp_blk, row_req, row_len, max_groups, num_rows)
+
+
+def m3s_prefill_rows(cu_q, seq_lens, num_rows: int, max_groups: int | None = None, dev_status=None,
+                     stream=None, out: Rows | None = None) -> Rows:
+    """Prefill row map and 64-row scan groups; max_groups defaults to the bound
+    ceil(num_rows / 64) + num_reqs (capped at MAX_GROUPS). ``out`` (a Rows from an
+    earlier call with the same sizes) is written in place."""
+    B, max_groups, rows = _prefill_rows_out(cu_q, seq_lens, num_rows, max_groups, out)
+    st = load().m3s_prefill_rows(_ptr(cu_q), _ptr(seq_lens), B, num_rows, max_groups, _ptr(rows.row_req),
+                                 _ptr(rows.row_len), _ptr(rows.grp_row), _ptr(rows.grp_req), _ptr(rows.grp_blk),
+                                 _ptr(dev_status), _stream(stream))
     _check("m3s_prefill_rows", st)
-    return out if out is not None else Rows(grp_row, grp_req, grp_blk, row_req, row_len, max_groups, num_rows)
+    return rows
+
+
+def m3s_store_and_prefill_rows(cache: Cache, k, v, idx, slot_mapping, cu_q, seq_lens, num_rows: int,
+                               max_groups: int | None = None, dev_status=None, stream=None,
+                               out: Rows | None = None) -> Rows:
+    """m3s_store and m3s_prefill_rows in one launch; returns the row map (``out``, from an
+    earlier call with the same sizes, is written in place)."""
+    torch = _torch()
+    ref = next(t for t in (k, v, idx) if t is not None)
+    T = ref.shape[0]
+    stride = ref.stride(0)
+    for name, t in (("k", k), ("v", v), ("idx", idx)):
+        if t is not None:
+            _need(t, name, torch.bfloat16)
+            if t.shape[0] != T or t.stride(0) != stride or t.stride(1) != 1 or t.shape[1] < HEAD_DIM:
+                raise ValueError(f"{name}: rows must share [T, >=128] shape and row stride")
+    _need(slot_mapping, "slot_mapping", torch.int32)
+    if slot_mapping.numel() != T or not slot_mapping.is_contiguous():
+        raise ValueError("slot_mapping must be a contiguous int32 [T]")
+    B, max_groups, rows = _prefill_rows_out(cu_q, seq_lens, num_rows, max_groups, out)
+    st = load().m3s_store_and_prefill_rows(cache.ref(), _ptr(k), _ptr(v), _ptr(idx), stride, _ptr(slot_mapping), T,
+                                           _ptr(cu_q), _ptr(seq_lens), B, num_rows, max_groups, _ptr(rows.row_req),
+                                           _ptr(rows.row_len), _ptr(rows.grp_row), _ptr(rows.grp_req),
+                                           _ptr(rows.grp_blk), _ptr(dev_status), _stream(stream))
+    _check("m3s_store_and_prefill_rows", st)
+    return rows
 
 
 def index_workspace(rows: Rows, max_blocks: int, topk: int, device="cuda"):

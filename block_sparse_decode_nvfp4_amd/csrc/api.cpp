@@ -159,6 +159,29 @@ m3s_status rows_args(RowsArgs& a, const int32_t* cu_q, const int32_t* seq_lens, 
   return M3S_OK;
 }
 
+m3s_status prefill_rows_args(RowsArgs& a, const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs,
+                             int32_t num_rows, int32_t max_groups, int32_t* row_req, int32_t* row_len,
+                             int32_t* grp_row, int32_t* grp_req, int32_t* grp_blk, uint32_t* dev_status) {
+  if (num_reqs < 0 || num_rows < 0) return M3S_ERR_INVALID_ARG;
+  if (num_reqs > M3S_MAX_REQS || num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
+  if (max_groups < 1 || max_groups > M3S_MAX_GROUPS) return M3S_ERR_UNSUPPORTED;
+  if (!cu_q || !grp_row || !grp_req || !grp_blk) return M3S_ERR_INVALID_ARG;
+  if (num_reqs > 0 && !seq_lens) return M3S_ERR_INVALID_ARG;
+  if (num_rows > 0 && (!row_req || !row_len)) return M3S_ERR_INVALID_ARG;
+  a.cu_q = cu_q;
+  a.seq_lens = seq_lens;
+  a.num_reqs = num_reqs;
+  a.num_rows = num_rows;
+  a.row_req = row_req;
+  a.row_len = row_len;
+  a.req_blk = grp_blk;
+  a.grp_row = grp_row;
+  a.grp_req = grp_req;
+  a.max_groups = max_groups;
+  a.status = dev_status;
+  return M3S_OK;
+}
+
 }  // namespace
 
 m3s_status m3s_store(const m3s_cache* cache, const uint16_t* k, const uint16_t* v, const uint16_t* idx_k,
@@ -256,25 +279,27 @@ m3s_status m3s_qknorm_rope_store(const m3s_cache* cache, const uint16_t* q, int6
 m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_t num_reqs, int32_t num_rows,
                             int32_t max_groups, int32_t* row_req, int32_t* row_len, int32_t* grp_row,
                             int32_t* grp_req, int32_t* grp_blk, uint32_t* dev_status, hipStream_t stream) {
-  if (num_reqs < 0 || num_rows < 0) return M3S_ERR_INVALID_ARG;
-  if (num_reqs > M3S_MAX_REQS || num_rows > M3S_MAX_ROWS) return M3S_ERR_UNSUPPORTED;
-  if (max_groups < 1 || max_groups > M3S_MAX_GROUPS) return M3S_ERR_UNSUPPORTED;
-  if (!cu_q || !grp_row || !grp_req || !grp_blk) return M3S_ERR_INVALID_ARG;
-  if (num_reqs > 0 && !seq_lens) return M3S_ERR_INVALID_ARG;
-  if (num_rows > 0 && (!row_req || !row_len)) return M3S_ERR_INVALID_ARG;
   RowsArgs a;
-  a.cu_q = cu_q;
-  a.seq_lens = seq_lens;
-  a.num_reqs = num_reqs;
-  a.num_rows = num_rows;
-  a.row_req = row_req;
-  a.row_len = row_len;
-  a.req_blk = grp_blk;
-  a.grp_row = grp_row;
-  a.grp_req = grp_req;
-  a.max_groups = max_groups;
-  a.status = dev_status;
+  const m3s_status st = prefill_rows_args(a, cu_q, seq_lens, num_reqs, num_rows, max_groups, row_req, row_len,
+                                          grp_row, grp_req, grp_blk, dev_status);
+  if (st != M3S_OK) return st;
   return from_hip(launch_prefill_rows(a, stream));
+}
+
+m3s_status m3s_store_and_prefill_rows(const m3s_cache* cache, const uint16_t* k, const uint16_t* v,
+                                      const uint16_t* idx_k, int64_t row_stride, const int32_t* slot_mapping,
+                                      int32_t num_tokens, const int32_t* cu_q, const int32_t* seq_lens,
+                                      int32_t num_reqs, int32_t num_rows, int32_t max_groups, int32_t* row_req,
+                                      int32_t* row_len, int32_t* grp_row, int32_t* grp_req, int32_t* grp_blk,
+                                      uint32_t* dev_status, hipStream_t stream) {
+  StoreArgs s;
+  m3s_status st = store_args(s, cache, k, v, idx_k, row_stride, slot_mapping, num_tokens, dev_status);
+  if (st != M3S_OK) return st;
+  RowsArgs r;
+  st = prefill_rows_args(r, cu_q, seq_lens, num_reqs, num_rows, max_groups, row_req, row_len, grp_row, grp_req,
+                         grp_blk, dev_status);
+  if (st != M3S_OK) return st;
+  return from_hip(launch_store_prefill_rows(s, r, stream));
 }
 
 }  // extern "C"

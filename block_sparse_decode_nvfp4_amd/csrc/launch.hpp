@@ -156,6 +156,7 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_decode_rows(const RowsArgs& a, hipStream_t stream);
 hipError_t launch_prefill_rows(const RowsArgs& a, hipStream_t stream);
 hipError_t launch_store_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t stream);
+hipError_t launch_store_prefill_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t stream);
 hipError_t launch_producer(const ProducerArgs& a, hipStream_t stream);
 hipError_t launch_index_topk(const IndexArgs& a, hipStream_t stream);
 hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream);

@@ -29,6 +29,16 @@ __global__ __launch_bounds__(256) void store_rows_kernel(StoreArgs s, RowsArgs r
   else decode_rows_body<256>(r, s_scan);
 }
 
+// Store and prefill row map in one launch: workgroups [0, store_grid) store, the last
+// one builds the prefill row map and the 64-row groups (its LDS, prefill_rows_lds_bytes
+// of the batch, is the launch's dynamic LDS).
+template <int FMT>
+__global__ __launch_bounds__(256) void store_prefill_rows_kernel(StoreArgs s, RowsArgs r, int store_grid) {
+  extern __shared__ int s_pref[];
+  if ((int)blockIdx.x < store_grid) store_body<FMT>(s, blockIdx.x);
+  else prefill_rows_body<256>(r, s_pref);
+}
+
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * 3;
   const int64_t grid = (rows + 15) / 16;
@@ -46,6 +56,16 @@ hipError_t launch_store_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t 
     hipLaunchKernelGGL(store_rows_kernel<1>, dim3((unsigned)grid + 1), dim3(256), 0, stream, s, r, (int)grid);
   else
     hipLaunchKernelGGL(store_rows_kernel<2>, dim3((unsigned)grid + 1), dim3(256), 0, stream, s, r, (int)grid);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_prefill_rows(const StoreArgs& s, const RowsArgs& r, hipStream_t stream) {
+  const int64_t grid = ((int64_t)s.num_tokens * 3 + 15) / 16;
+  const size_t lds = prefill_rows_lds_bytes(r.num_reqs);
+  if (s.format == 1)
+    hipLaunchKernelGGL(store_prefill_rows_kernel<1>, dim3((unsigned)grid + 1), dim3(256), lds, stream, s, r, (int)grid);
+  else
+    hipLaunchKernelGGL(store_prefill_rows_kernel<2>, dim3((unsigned)grid + 1), dim3(256), lds, stream, s, r, (int)grid);
   return hipGetLastError();
 }
 

@@ -282,6 +282,21 @@ m3s_status m3s_prefill_rows(const int32_t* cu_q, const int32_t* seq_lens, int32_
                             hipStream_t stream);
 
 /*
+ * m3s_store_and_prefill_rows - m3s_store and m3s_prefill_rows in one launch (the
+ * two are independent: the store writes the planes, the row map its own arrays),
+ * for a prefill chunk's step. Arguments, validation, results and status bits are
+ * those of the two calls; a call that would fail either of them launches nothing.
+ * It saves one launch of a step whose store and row map are each mostly launch and
+ * first-load latency ([ATOM-2744] Design, Write path: the store is launch-bound).
+ */
+m3s_status m3s_store_and_prefill_rows(const m3s_cache* cache, const uint16_t* k, const uint16_t* v,
+                                      const uint16_t* idx_k, int64_t row_stride, const int32_t* slot_mapping,
+                                      int32_t num_tokens, const int32_t* cu_q, const int32_t* seq_lens,
+                                      int32_t num_reqs, int32_t num_rows, int32_t max_groups, int32_t* row_req,
+                                      int32_t* row_len, int32_t* grp_row, int32_t* grp_req, int32_t* grp_blk,
+                                      uint32_t* dev_status, hipStream_t stream);
+
+/*
  * m3s_index_topk - [ATOM-2744] Design, Index and Decode score grid, and Fused
  * verify top-k: score every causal 128-token block of every row against the
  * FP4 index cache (reached through the block table) and keep the top-k.

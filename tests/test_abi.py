@@ -197,6 +197,23 @@ def test_store_and_rows_validation(lib):
     assert f(rb=None) == E.ERR_INVALID_ARG
 
 
+def test_store_and_prefill_rows_validation(lib):
+    """The one-launch store and prefill row map refuses what either call refuses."""
+    E = m3s
+    f = lambda cache=None, k=FAKE, stride=128, slots=FAKE, T=1, cu=FAKE, seq=FAKE, B=1, R=1, G=4, gb=FAKE: \
+        lib.m3s_store_and_prefill_rows(ctypes.byref(_cache() if cache is None else cache), k, None, None, stride,
+                                       slots, T, cu, seq, B, R, G, FAKE, FAKE, FAKE, FAKE, gb, None, None)
+    assert f(T=-1) == E.ERR_INVALID_ARG
+    assert f(slots=None) == E.ERR_INVALID_ARG
+    assert f(stride=100) == E.ERR_INVALID_ARG
+    assert f(cache=_cache(page=64)) == E.ERR_UNSUPPORTED
+    assert f(B=-1) == E.ERR_INVALID_ARG
+    assert f(B=4097) == E.ERR_UNSUPPORTED
+    assert f(G=0) == E.ERR_UNSUPPORTED
+    assert f(cu=None) == E.ERR_INVALID_ARG
+    assert f(gb=None) == E.ERR_INVALID_ARG
+
+
 def test_qknorm_rope_store_validation(lib):
     """Every call below fails host validation (or has no tokens) and launches nothing."""
     MIS = ctypes.c_void_p(4096 + 8)      # 8-byte aligned only

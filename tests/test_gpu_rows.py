@@ -150,3 +150,40 @@ def test_store_and_rows_equals_separate_calls(gpu, fmt):
     assert all(torch.equal(u, w) for u, w in zip(pa, pb))
     assert torch.equal(ra, rb_) and torch.equal(la, lb) and torch.equal(ba, bb)
     assert sa == sb and sa & gpu.DEV_BITS["BAD_SLOT"] and sa & gpu.DEV_BITS["BAD_ROWS"]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_store_and_prefill_rows_equals_separate_calls(gpu, fmt):
+    """One launch for store + prefill row map writes what m3s_store and m3s_prefill_rows
+    write, status bits included (a slot past the cache; chunks of 300, 1, 64, 65 and 700
+    rows, one request with fewer tokens than rows)."""
+    rng = np.random.default_rng(21)
+    ql = np.array([300, 1, 64, 65, 700], dtype=np.int64)
+    seq_np = ql + rng.integers(0, 9000, size=len(ql))
+    seq_np[1] = 0            # fewer tokens than rows: rejected
+    T, P = int(ql.sum()), 16
+    g = torch.Generator(device="cpu").manual_seed(4)
+    x = (torch.randn((3, T, 128), generator=g) * 3).to(torch.bfloat16).to(DEV)
+    slots = torch.as_tensor(rng.permutation(P * 128)[:T].astype(np.int32), device=DEV)
+    slots[11] = P * 128 + 3  # bad slot
+    cu = torch.as_tensor(np.concatenate([[0], np.cumsum(ql)]).astype(np.int32), device=DEV)
+    seq = torch.as_tensor(seq_np.astype(np.int32), device=DEV)
+    R = T + 7
+    outs = []
+    for fused in (False, True):
+        c = gpu.Cache(fmt, P, DEV)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        if fused:
+            rows = gpu.m3s_store_and_prefill_rows(c, x[0], x[1], x[2], slots, cu, seq, R, dev_status=st)
+        else:
+            gpu.m3s_store(c, x[0], x[1], x[2], slots, st)
+            rows = gpu.m3s_prefill_rows(cu, seq, R, dev_status=st)
+        torch.cuda.synchronize()
+        outs.append(([t.cpu() for pl in c.planes.values() for t in pl],
+                     [t.cpu() for t in (rows.row_req, rows.row_len, rows.grp_row, rows.grp_req, rows.grp_blk)],
+                     int(st.item())))
+    (pa, ra, sa), (pb, rb_, sb) = outs
+    assert all(torch.equal(u, w) for u, w in zip(pa, pb))
+    assert all(torch.equal(u, w) for u, w in zip(ra, rb_))
+    assert sa == sb and sa & gpu.DEV_BITS["BAD_SLOT"] and sa & gpu.DEV_BITS["BAD_ROWS"]
+
