@@ -42,44 +42,47 @@ __global__ __launch_bounds__(kWaves * 64, REPS == 1 ? 1 : 4) void attend_split_k
   attend_split_body<FMT, REPS>(a, r, sp, sh, nullptr, nullptr, 0, 0);
 }
 
-// All partials of the row are loaded before any is used (one round trip);
-// nsplit <= kMaxSplits.
+// All partials of the row are loaded before any is used (one round trip): NS
+// (4 or 16, >= nsplit) loads per thread with no branch between them, split s past
+// nsplit reading split 0 again (unused). Loads guarded by a branch each were issued
+// one round trip after another: the compiler waited for each split's (m, l) before
+// the branch to the next split's loads.
 constexpr int kMaxSplits = (64 + kBlocks - 1) / kBlocks;
 
+template <int NS>
 __global__ __launch_bounds__(256) void attend_combine_kernel(AttendArgs a) {
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int hh = tid >> 4, d0 = (tid & 15) * 8;
   if (hh >= a.num_heads) return;
-  float mv[kMaxSplits], lv[kMaxSplits];
-  f32x4 ov[kMaxSplits][2];
+  const int ns = a.nsplit;
+  float mv[NS], lv[NS];
+  f32x4 ov[NS][2];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < a.nsplit) {
-      const float* ml = a.part_ml + (((int64_t)r * a.nsplit + s) * 16 + hh) * 2;
-      const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + (((int64_t)r * a.nsplit + s) * 16 + hh) * kDim + d0);
-      mv[s] = ml[0];
-      lv[s] = ml[1];
-      ov[s][0] = po[0];
-      ov[s][1] = po[1];
-    }
+  for (int s = 0; s < NS; ++s) {
+    const int sl = s < ns ? s : 0;
+    const float* ml = a.part_ml + (((int64_t)r * ns + sl) * 16 + hh) * 2;
+    const f32x4* po = reinterpret_cast<const f32x4*>(a.part_o + (((int64_t)r * ns + sl) * 16 + hh) * kDim + d0);
+    mv[s] = ml[0];
+    lv[s] = ml[1];
+    ov[s][0] = po[0];
+    ov[s][1] = po[1];
   }
+  // no branch between the loads and their use either (a branch lets the compiler sink
+  // the O loads past the wait for m): splits past nsplit get weight 0, and a row with
+  // no causal token (every m = -inf) gets weights 2^-inf = 0
   float M = -INFINITY;
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s)
-    if (s < a.nsplit) M = fmaxf(M, mv[s]);
+  for (int s = 0; s < NS; ++s) M = fmaxf(M, s < ns ? mv[s] : -INFINITY);
+  const float Mr = M == -INFINITY ? 0.f : M;
   float L = 0.f;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
 #pragma unroll
-    for (int s = 0; s < kMaxSplits; ++s) {
-      if (s < a.nsplit) {
-        const float f = __builtin_amdgcn_exp2f(mv[s] - M);
-        L += f * lv[s];
-        acc0 += f * ov[s][0];
-        acc1 += f * ov[s][1];
-      }
-    }
+  for (int s = 0; s < NS; ++s) {
+    const float f = s < ns ? __builtin_amdgcn_exp2f(mv[s] - Mr) : 0.f;
+    L += f * lv[s];
+    acc0 += f * ov[s][0];
+    acc1 += f * ov[s][1];
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   f32x4* dst = reinterpret_cast<f32x4*>(a.out + ((int64_t)r * a.num_heads + hh) * kDim + d0);
@@ -129,7 +132,10 @@ hipError_t launch_sparse_attend(const AttendArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_attend_combine(const AttendArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(attend_combine_kernel, dim3((unsigned)a.num_rows), dim3(256), 0, stream, a);
+  if (a.nsplit <= 4)
+    hipLaunchKernelGGL(attend_combine_kernel<4>, dim3((unsigned)a.num_rows), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attend_combine_kernel<kMaxSplits>, dim3((unsigned)a.num_rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
