@@ -659,6 +659,9 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
   __shared__ int s_unit[kScanChunk];  // request * kMaxBlocks + block; -1: not scored
   __shared__ int s_page[kScanChunk];  // page; -1: unusable
   __shared__ int s_ctr;
+  // prefill groups' requests, read with the block prefix (no dependent load before a
+  // unit's block-table entry)
+  __shared__ int s_greq[NT > 1 ? M3S_MAX_REQS_INTERNAL : 1];
   // decode step: cu_q and the rows' length base, read by the prefix anyway; a wave
   // that meets a new request issues its query loads from these, with no dependent
   // global load first (under the scan's load that round trip takes microseconds).
@@ -680,7 +683,10 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
     static_assert(NT == 1 && H == 1, "the decode step's scan");
     if (tid < 64) step_prefix_old(a, s_blk, s_cq, s_sb);
   } else {
-    for (int i = tid; i <= B; i += kScanWaves * 64) s_blk[i] = a.req_blk[i];
+    for (int i = tid; i <= B; i += kScanWaves * 64) {
+      s_blk[i] = a.req_blk[i];
+      if (NT > 1 && i < B) s_greq[i] = a.grp_req ? a.grp_req[i] : i;
+    }
   }
   __syncthreads();
   const int64_t total = (int64_t)s_blk[B] * H;
@@ -726,10 +732,18 @@ __device__ __forceinline__ void scan_body(const IndexArgs& a, int wg, int nwg) {
       int key = -1, pg = -1;
       if (jl < a.max_blocks) {
         key = (bl * H + half) * kMaxBlocks + jl;
-        // rows past the query tiles' capacity are never scored: flag the group
-        if (jl == 0 && half == 0 && a.cu_q[bl + 1] - a.cu_q[bl] > 16 * NT * H) set_status(a.status, kDevBadRows);
-        const int breq = a.grp_req ? a.grp_req[bl] : bl;  // the group's request
+        // the page first: its load goes out before the checks below, which would hold it
+        // back a round trip (a status atomic may not be passed by a later load)
+        int breq = bl;  // the group's request
+        if constexpr (NT > 1) breq = s_greq[bl];
         pg = breq >= 0 ? a.block_table[(int64_t)breq * a.bt_stride + jl] : -1;
+        // rows past the query tiles' capacity are never scored: flag the group
+        bool over = false;
+        if (jl == 0 && half == 0) {
+          if constexpr (STEP) over = s_cq[bl + 1] - s_cq[bl] > 16 * NT * H;
+          else over = a.cu_q[bl + 1] - a.cu_q[bl] > 16 * NT * H;
+        }
+        if (over) set_status(a.status, kDevBadRows);
         if (pg < 0 || pg >= a.num_pages) {
           set_status(a.status, kDevBadPage);
           pg = -1;
