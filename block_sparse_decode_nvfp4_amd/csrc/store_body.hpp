@@ -19,8 +19,15 @@ struct StoreLoad {
   int32_t slot;  // -1: not loaded
 };
 
+// The row's tensor pointers are chosen among values held in scalar registers: left to
+// the compiler, the choice by a per-lane index became a vector load from the kernel's
+// argument block, a dependent round trip ahead of the row's own loads.
 __device__ __forceinline__ const uint16_t* store_src(const StoreArgs& a, int ten) {
-  return ten == 0 ? a.k : (ten == 1 ? a.v : a.idx);
+  const uint16_t* k = a.k;
+  const uint16_t* v = a.v;
+  const uint16_t* x = a.idx;
+  asm volatile("" : "+s"(k), "+s"(v), "+s"(x));
+  return ten == 0 ? k : (ten == 1 ? v : x);
 }
 
 // Loads of row rr (rr < 0: none). Every lane of the row's 16-lane group calls it.
@@ -57,8 +64,15 @@ __device__ __forceinline__ void store_commit(const StoreArgs& a, int lane16, con
   uint32_t packed, scale_byte;
   quantize_lane<FMT>(bits, packed, scale_byte);
   if (live) {
-    uint8_t* dd = ten == 0 ? a.k_data : (ten == 1 ? a.v_data : a.idx_data);
-    uint8_t* ds = ten == 0 ? a.k_scale : (ten == 1 ? a.v_scale : a.idx_scale);
+    uint8_t* kd = a.k_data;
+    uint8_t* vd = a.v_data;
+    uint8_t* xd = a.idx_data;
+    uint8_t* ks = a.k_scale;
+    uint8_t* vs = a.v_scale;
+    uint8_t* xs = a.idx_scale;
+    asm volatile("" : "+s"(kd), "+s"(vd), "+s"(xd), "+s"(ks), "+s"(vs), "+s"(xs));
+    uint8_t* dd = ten == 0 ? kd : (ten == 1 ? vd : xd);
+    uint8_t* ds = ten == 0 ? ks : (ten == 1 ? vs : xs);
     write_lane<FMT>(dd, ds, ld.slot, lane16, packed, scale_byte);
   }
 }
