@@ -96,8 +96,10 @@ __device__ __forceinline__ void row_split_of(int b, int nsplit, int num_rows, in
 // sel_pages when the select wrote them (loaded beside the ids: no dependent
 // lookup), or, when s_ids is given (the select ran in the same workgroup), the
 // ids, their pages and the row's request and length come from the caller (LDS /
-// registers).
-template <int FMT, int REPS = 1>
+// registers). LDS_IDS: the caller passes s_ids (the fused kernel); the paths that read
+// the ids and pages from global memory are then not compiled, so no wait for them (or
+// for the query loads issued before them) stands between the ids and the K/V loads.
+template <int FMT, int REPS = 1, bool LDS_IDS = false>
 __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, int sp, AttendShared& sh,
                                                   const int* s_ids, const int* s_pages, int b_in, int len_in) {
   constexpr int SB = FMT == 1 ? 8 : 4;
@@ -108,14 +110,19 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
 
   // ---- which blocks this wave attends; the row map, the ids and the query are
   // independent loads, issued together
-  const int b = s_ids ? b_in : a.row_req[r];
-  const int len = s_ids ? len_in : a.row_len[r];
+  const int b = LDS_IDS ? b_in : a.row_req[r];
+  const int len = LDS_IDS ? len_in : a.row_len[r];
   int id[REPS], pg_sel[REPS];
 #pragma unroll
   for (int rep = 0; rep < REPS; ++rep) {
     const int slot = (sp * REPS + rep) * kBlocks + w / kHalves;
-    id[rep] = slot < a.topk ? (s_ids ? s_ids[slot] : a.topk_ids[(int64_t)r * a.topk + slot]) : -1;
-    pg_sel[rep] = (!s_ids && a.sel_pages && slot < a.topk) ? a.sel_pages[(int64_t)r * a.topk + slot] : -1;
+    if constexpr (LDS_IDS) {
+      id[rep] = slot < a.topk ? s_ids[slot] : -1;
+      pg_sel[rep] = -1;
+    } else {
+      id[rep] = slot < a.topk ? a.topk_ids[(int64_t)r * a.topk + slot] : -1;
+      pg_sel[rep] = (a.sel_pages && slot < a.topk) ? a.sel_pages[(int64_t)r * a.topk + slot] : -1;
+    }
   }
   u32x4 raw[4] = {};
   if (n < a.num_heads) {
@@ -135,8 +142,9 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
         if (id[rep] >= nbr || id[rep] >= a.max_blocks) {
           if (lane == 0) set_status(a.status, kDevBadBlockId);
         } else {
-          const int pg = s_ids ? s_pages[slot]
-                               : (a.sel_pages ? pg_sel[rep] : a.block_table[(int64_t)b * a.bt_stride + id[rep]]);
+          int pg;
+          if constexpr (LDS_IDS) pg = s_pages[slot];
+          else pg = a.sel_pages ? pg_sel[rep] : a.block_table[(int64_t)b * a.bt_stride + id[rep]];
           if (pg < 0 || pg >= a.num_pages) {
             if (lane == 0) set_status(a.status, kDevBadPage);
           } else {
@@ -149,33 +157,39 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
   }
 
   // ---- query heads as the B operand, the same for all of the wave's blocks: NVFP4
-  // scaled by 2^P into fp16 range (built once here); MXFP4 the bf16 values as they are
+  // scaled by 2^P into fp16 range (built once per wave); MXFP4 the bf16 values as they
+  // are. With one block per wave it is built after the block's K/V loads are issued,
+  // so that waiting for the query does not hold them back; with several blocks, before
+  // the first block (measured faster there).
   typedef typename Dec::op_t op_t;
   op_t qop[4];
   float c = 0.f;  // logits in log2 units: x = S' * c
-  if constexpr (FMT == 1) {
-    uint32_t mx = 0;
+  auto build_qop = [&]() {
+    if constexpr (FMT == 1) {
+      uint32_t mx = 0;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
-    mx = lane_max<1, 64>(mx);
-    int P = 0;
-    if (mx) {
-      const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
-      const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
-      P = 13 - fl;
-      P = P > 64 ? 64 : (P < -64 ? -64 : P);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
-        qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
+        for (int q4 = 0; q4 < 4; ++q4) mx = max(mx, max(raw[s][q4] & 0x7FFFu, (raw[s][q4] >> 16) & 0x7FFFu));
+      mx = lane_max<1, 64>(mx);
+      int P = 0;
+      if (mx) {
+        const uint32_t ex = mx >> 7, mant = mx & 0x7Fu;
+        const int fl = ex ? (int)ex - 127 : (31 - __builtin_clz(mant)) - 133;
+        P = 13 - fl;
+        P = P > 64 ? 64 : (P < -64 ? -64 : P);
       }
-    c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
-  }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t bits = (e & 1) ? (raw[s][e >> 1] >> 16) : (raw[s][e >> 1] & 0xFFFFu);
+          qop[s][e] = (_Float16)__builtin_ldexpf(bf16_bits_to_f32(bits), P);
+        }
+      c = a.sm_scale * 1.4426950408889634f * __builtin_ldexpf(1.0f, -P);
+    }
+  };
+  if constexpr (REPS > 1) build_qop();
 
   float m_run = -INFINITY, l_run = 0.f;  // per head n (replicated over G)
   f32x4 o[8];
@@ -217,6 +231,7 @@ __device__ __forceinline__ void attend_split_body(const AttendArgs& a, int r, in
         else vs[i] = vsp[(t0 + 16 * i + n) * SB + G];
       }
 
+      if constexpr (REPS == 1) build_qop();
       if constexpr (FMT == 2) {  // MXFP4: the bf16 words as they are, set per block (set once before the loop, the two-block build spills)
 #pragma unroll
         for (int s = 0; s < 4; ++s) qop[s] = __builtin_bit_cast(bf16x8, raw[s]);

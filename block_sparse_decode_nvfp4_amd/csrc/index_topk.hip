@@ -1521,7 +1521,7 @@ __global__ __launch_bounds__(kWaves * 64) void select_attend_kernel(IndexArgs ia
   const int sp = blockIdx.x - r * aa.nsplit;
   select_row<FMT, PER, kWaves, true>(ia, r, u.s, sp == 0, s_ids, s_pages, s_row);
   __syncthreads();
-  attend_split_body<FMT>(aa, r, sp, u.t, s_ids, s_pages, s_row[0], s_row[1]);
+  attend_split_body<FMT, 1, true>(aa, r, sp, u.t, s_ids, s_pages, s_row[0], s_row[1]);
 }
 
 size_t index_ws_bytes(int32_t num_rows, int32_t max_blocks) {
